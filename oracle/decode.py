@@ -1,0 +1,195 @@
+"""Oracle decode: block loop, cache policy and confidence-threshold commit, in fp64 NumPy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What it follows
+---------------
+* Generation is split into blocks of ``block_size`` that are denoised left to
+  right; only the current block's masked positions can be committed
+  (Fast-dLLM README, Quick Start: ``--gen_length --steps --block_size``;
+  ES-dLLM paper card, Streaming-dLLM abstract: "block-wise diffusion process").
+* Confidence-threshold parallel decoding: in one step every masked position of
+  the block whose confidence clears the threshold is committed, and a
+  committed token is never revised ("Fast-dLLM: Four Acceleration Tracks ...",
+  section "The v1 Mechanism"; README Dream command ``alg=confidence_threshold,
+  threshold=0.9``).  "Clears" is read as strictly greater.
+* The fixed schedule stays as a floor: step j of a block commits at least
+  k_j of the most confident masked positions, with the block's step budget
+  ``steps / n_blocks`` split evenly over its positions ("... Four Acceleration
+  Tracks ...", section "Fast-dLLM v1 Versus a Standard Diffusion Sampler": v1
+  keeps the conventional schedule and commits confident positions before it
+  ends).  With the default ``steps = gen_length`` the floor is one position per
+  step.  Ties in confidence go to the lower position; NaN confidence ranks last.
+* The cache is refreshed only at block boundaries: the first step of every
+  block is a full forward that rewrites every cache slot and whose block-row
+  statistics are that step's statistics.  Later steps of the block recompute
+  only the block rows (dual cache) or the block and every later row (prefix
+  cache), and attend to the cached K/V of the others.  With no cache every
+  step is a full forward (Streaming-dLLM README tables: "Prefix-Cache" and
+  "Fast-dLLM" columns against the no-cache backbone).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .model import Model
+
+__all__ = ["steps_per_block", "floor_count", "commit_set", "Decoder"]
+
+NO_CACHE, PREFIX_CACHE, DUAL_CACHE = 0, 1, 2
+
+
+def steps_per_block(gen_length: int, block_size: int, steps: int) -> int:
+    """Step budget of one block: steps / n_blocks (steps = 0 means gen_length)."""
+    if gen_length % block_size:
+        raise ValueError("gen_length must be a multiple of block_size")
+    nb = gen_length // block_size
+    steps = steps or gen_length
+    if steps % nb:
+        raise ValueError("steps must be a multiple of the number of blocks")
+    return steps // nb
+
+
+def floor_count(block_size: int, spb: int, j: int) -> int:
+    """How many positions step j of a block commits at least: the block's positions
+    spread evenly over its spb steps, the remainder going to the earliest steps."""
+    base, extra = divmod(block_size, spb)
+    return max(1, base + (1 if j < extra else 0))
+
+
+def commit_set(masked: np.ndarray, conf: np.ndarray, threshold: float, k: int) -> np.ndarray:
+    """Positions to commit: every masked one with conf > threshold, plus the k most
+    confident masked ones (conf descending, then position ascending)."""
+    n = masked.shape[0]
+    out = np.zeros(n, dtype=bool)
+    idx = [i for i in range(n) if masked[i]]
+    if not idx:
+        return out
+    c = {i: (-np.inf if np.isnan(conf[i]) else float(conf[i])) for i in idx}
+    for i in idx:
+        if c[i] > threshold:
+            out[i] = True
+    ranked = sorted(idx, key=lambda i: (-c[i], i))
+    for i in ranked[:k]:
+        out[i] = True
+    return out
+
+
+class Decoder:
+    """Block-wise cached decoding of a batch of independent sequences.
+
+    State: tokens ``x`` [B, L], one KV cache per sequence, the current block and
+    the step index inside it.  Batch rows advance in lockstep: a row whose block
+    is finished commits nothing until every row has finished the block.
+    """
+
+    def __init__(self, model: Model, refresh_every_step: bool = False, keep_logits: bool = False):
+        cfg = model.cfg
+        self.m = model
+        self.cfg = cfg
+        self.B = cfg["batch"]
+        self.P = cfg["prompt_len"]
+        self.Bs = cfg["block_size"]
+        self.L = cfg["prompt_len"] + cfg["gen_length"]
+        self.nb = cfg["gen_length"] // cfg["block_size"]
+        self.spb = steps_per_block(cfg["gen_length"], cfg["block_size"], cfg["steps"])
+        self.mask_id = cfg["mask_id"]
+        self.refresh_every_step = refresh_every_step
+        self.keep_logits = keep_logits
+        self.caches = [model.new_cache() for _ in range(self.B)]
+        self.x = None
+        self.block = -1
+        self.j = 0
+        self.pending = None
+        self.forwards = {"full": 0, "cached": 0}
+
+    # -- state ---------------------------------------------------------------------------
+    def set_tokens(self, x: np.ndarray) -> None:
+        x = np.asarray(x, dtype=np.int64)
+        assert x.shape == (self.B, self.L)
+        self.x = x.copy()
+
+    def block_range(self, b: int) -> tuple[int, int]:
+        s = self.P + b * self.Bs
+        return s, s + self.Bs
+
+    # -- forwards ------------------------------------------------------------------------
+    def _full(self) -> list:
+        s, e = self.block_range(self.block)
+        out = []
+        for r in range(self.B):
+            h = self.m.forward(self.x[r], 0, self.L, self.caches[r])
+            out.append(self.m.stats(h[s:e]))
+        self.forwards["full"] += 1
+        return out
+
+    def _cached(self) -> list:
+        s, e = self.block_range(self.block)
+        mode = self.cfg["use_cache"]
+        stop = e if mode == DUAL_CACHE else self.L
+        out = []
+        for r in range(self.B):
+            h = self.m.forward(self.x[r], s, stop, self.caches[r])
+            out.append(self.m.stats(h[:self.Bs]))
+        self.forwards["cached"] += 1
+        return out
+
+    def block_begin(self, b: int) -> None:
+        """Refresh at a block boundary: full forward, all cache slots rewritten;
+        its block-row statistics serve the block's first step."""
+        if not 0 <= b < self.nb:
+            raise ValueError("block out of range")
+        self.block, self.j = b, 0
+        self.pending = self._full()
+
+    def step(self) -> tuple[dict, bool]:
+        """One denoising step of the current block: statistics, then commit.
+
+        Returns the step record and whether every row's block is finished.
+        """
+        if self.pending is not None:
+            stats, self.pending = self.pending, None
+        elif self.refresh_every_step or self.cfg["use_cache"] == NO_CACHE:
+            stats = self._full()
+        else:
+            stats = self._cached()
+        s, e = self.block_range(self.block)
+        k = floor_count(self.Bs, self.spb, self.j)
+        committed = np.zeros((self.B, self.Bs), dtype=bool)
+        for r in range(self.B):
+            masked = self.x[r, s:e] == self.mask_id
+            c = commit_set(masked, stats[r]["conf"], self.cfg["threshold"], k)
+            self.x[r, s:e][c] = stats[r]["tok"][c]
+            committed[r] = c
+        rec = dict(block=self.block, j=self.j, k=k,
+                   tok=np.stack([st["tok"] for st in stats]),
+                   conf=np.stack([st["conf"] for st in stats]),
+                   p2=np.stack([st["p2"] for st in stats]),
+                   committed=committed, x=self.x.copy())
+        if self.keep_logits:
+            rec["logits"] = np.stack([st["logits"] for st in stats])
+        self.j += 1
+        done = not bool((self.x[:, s:e] == self.mask_id).any())
+        return rec, done
+
+    def run_block(self, b: int) -> list:
+        """block_begin(b), then steps until the block is finished."""
+        self.block_begin(b)
+        recs = []
+        while True:
+            rec, done = self.step()
+            recs.append(rec)
+            if done:
+                return recs
+
+    def generate(self, prompt: np.ndarray):
+        """x = [prompt | mask^G]; every block in order.  Returns (x, step records)."""
+        prompt = np.asarray(prompt, dtype=np.int64)
+        x = np.full((self.B, self.L), self.mask_id, dtype=np.int64)
+        x[:, :self.P] = prompt
+        self.set_tokens(x)
+        recs = []
+        for b in range(self.nb):
+            recs += self.run_block(b)
+        return self.x.copy(), recs
