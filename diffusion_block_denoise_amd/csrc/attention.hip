@@ -1,0 +1,278 @@
+// Non-causal attention of a row set's queries over every cached position, with grouped K/V heads.
+//
+// bf16 path (v_mfma_f32_32x32x16_bf16), one wave per tile of 32 query rows of one (batch row,
+// K/V head) pair.  Query rows of a pair are (position, head-in-group) combinations, so a group
+// of G query heads shares every K/V load.  The wave computes S^T = K Q^T over 32 keys at a time:
+// in the MFMA output each lane holds one query and 16 keys, so the row softmax needs a single
+// cross-half shuffle.  The probabilities P^T (rounded to bf16) are already laid out as the B
+// operand of the next MFMA, O^T += V^T P^T, whose A operand comes from the transposed V cache
+// ([hd][L] per head): every lane reads two runs of four consecutive keys.  No LDS is used.
+// The normaliser sums the rounded probabilities, so the weights applied to V sum to one.
+// When the tiles alone cannot fill the GPU (a cached step has few queries) the keys are split
+// into chunks; each chunk writes (O, running max, sum) and a merge kernel combines the chunks
+// in chunk order.
+//
+// f32 path: one workgroup per (query row, head): scores in LDS, then weights times V.
+#include "kernels.h"
+
+namespace dllm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+static inline int attn_tiles(RowSet rs, int H, int Hkv) {
+  return (rs.nR * (H / Hkv) + 31) / 32;
+}
+
+static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk) {
+  const long waves = (long)attn_tiles(rs, H, Hkv) * rs.B * Hkv;
+  const int kt = rs.Lp / 32;  // 32-key tiles
+  int want = (int)((256 + waves - 1) / waves);
+  if (want > kt) want = kt;
+  if (want < 1) want = 1;
+  chunk = (kt + want - 1) / want * 32;
+  splits = (rs.Lp + chunk - 1) / chunk;
+}
+
+size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
+  if (dtype == 0) return 0;
+  int splits, chunk;
+  attn_plan(rs, H, Hkv, splits, chunk);
+  if (splits == 1) return 0;
+  return (size_t)splits * rs.B * Hkv * attn_tiles(rs, H, Hkv) * 32 * (hd + 2) * sizeof(float);
+}
+
+template <int HD>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ q,
+                                                       const bf16 *__restrict__ kc,
+                                                       const bf16 *__restrict__ vt, RowSet rs,
+                                                       int H, int Hkv, int chunk, float scale_log2,
+                                                       bf16 *o_hi, bf16 *o_lo, float *part) {
+  constexpr int KS = HD / 16;  // k-steps of the QK^T product
+  constexpr int DB = HD / 32;  // 32-dim blocks of the output
+  const int G = H / Hkv;
+  const int nrows = rs.nR * G;
+  const int qt = blockIdx.x, bg = blockIdx.y, split = blockIdx.z;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+
+  const int r = qt * 32 + col;
+  const bool valid = r < nrows;
+  const int pi = valid ? r / G : 0;
+  const int head = g * G + (valid ? r % G : 0);
+  const int m = b * rs.nR + pi;
+  const int ldq = H * HD;
+
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (valid) {
+      qf[kk] = *(const bf16x8_t *)(q + (size_t)m * ldq + head * HD + kk * 16 + half * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+    }
+  }
+  const bf16 *K = kc + (size_t)bg * rs.Lp * HD;
+  const bf16 *V = vt + (size_t)bg * HD * rs.Lp;
+
+  float mrun = -INFINITY, lsum = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+
+  const int kbeg = split * chunk;
+  const int kend = min(rs.Lp, kbeg + chunk);
+  for (int kb = kbeg; kb < kend; kb += 32) {
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    const bf16 *krow = K + (size_t)(kb + col) * HD + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8_t kf = *(const bf16x8_t *)(krow + kk * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+    }
+    // s[i]: key kb + 8*(i/4) + 4*half + i%4, query col
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+      s[i] = key < rs.L ? s[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, s[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+    bf16x8_t pf[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const __bf16 pb = (__bf16)exp2f(s[i] - mnew);
+      pf[i >> 3][i & 7] = pb;
+      psum += (float)pb;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    lsum = lsum * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      const bf16 *vrow = V + (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x4_t v0 = *(const bf16x4_t *)(vrow + 16 * ks);
+        const bf16x4_t v1 = *(const bf16x4_t *)(vrow + 16 * ks + 8);
+        bf16x8_t vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { vf[e] = v0[e]; vf[e + 4] = v1[e]; }
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[d], 0, 0, 0);
+      }
+    }
+  }
+  if (!valid) return;
+  // o[d][i]: dim d*32 + 8*(i/4) + 4*half + i%4 of query col
+  if (gridDim.z == 1) {
+    const float inv = 1.0f / lsum;
+    bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
+    bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const float v = o[d][i] * inv;
+        const bf16 hi = __float2bfloat16(v);
+        oh[dim] = hi;
+        ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+      }
+  } else {
+    // part[split][bg][qt][col][HD + 2]
+    float *pp = part + ((((size_t)split * gridDim.y + bg) * gridDim.x + qt) * 32 + col) * (HD + 2);
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pp[d * 32 + 8 * (i >> 2) + 4 * half + (i & 3)] = o[d][i];
+    if (half == 0) {
+      pp[HD] = mrun;
+      pp[HD + 1] = lsum;
+    }
+  }
+}
+
+// Combine the key chunks: one wave per query row slot, lanes over dims.
+template <int HD>
+__global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict__ part, RowSet rs,
+                                                        int H, int Hkv, int n_qt, int splits,
+                                                        bf16 *o_hi, bf16 *o_lo) {
+  const int G = H / Hkv;
+  const int slot = blockIdx.x;  // (bg, qt, col)
+  const int col = slot % 32, qt = (slot / 32) % n_qt, bg = slot / 32 / n_qt;
+  const int r = qt * 32 + col;
+  if (r >= rs.nR * G) return;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int m = b * rs.nR + r / G, head = g * G + r % G;
+  const size_t stride = (size_t)rs.B * Hkv * n_qt * 32 * (HD + 2);
+  const float *p0 = part + (((size_t)bg * n_qt + qt) * 32 + col) * (HD + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, p0[s * stride + HD]);
+  float l = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = p0[s * stride + HD];
+    if (ms > -INFINITY) l += p0[s * stride + HD + 1] * exp2f(ms - mx);
+  }
+  const float inv = 1.0f / l;
+  for (int dim = threadIdx.x; dim < HD; dim += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ms = p0[s * stride + HD];
+      if (ms > -INFINITY) acc += p0[s * stride + dim] * exp2f(ms - mx);
+    }
+    const float v = acc * inv;
+    const size_t o = (size_t)m * H * HD + head * HD + dim;
+    const bf16 hi = __float2bfloat16(v);
+    o_hi[o] = hi;
+    o_lo[o] = __float2bfloat16(v - __bfloat162float(hi));
+  }
+}
+
+// fp32: one workgroup of 64 per (row m, head).  Dynamic LDS: Lp scores.
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ q,
+                                                      const float *__restrict__ kc,
+                                                      const float *__restrict__ vt, RowSet rs,
+                                                      int H, int Hkv, int hd, float scale,
+                                                      float *o) {
+  extern __shared__ float sc[];
+  const int m = blockIdx.x, head = blockIdx.y;
+  const int b = m / rs.nR;
+  const int g = head / (H / Hkv);
+  const float *qr = q + (size_t)m * H * hd + head * hd;
+  const float *K = kc + ((size_t)b * Hkv + g) * rs.Lp * hd;
+  const float *V = vt + ((size_t)b * Hkv + g) * hd * rs.Lp;
+  const int lane = threadIdx.x;
+  float mx = -INFINITY;
+  for (int key = lane; key < rs.L; key += 64) {
+    float s = 0.f;
+    for (int d = 0; d < hd; ++d) s = fmaf(qr[d], K[(size_t)key * hd + d], s);
+    s *= scale;
+    sc[key] = s;
+    mx = fmaxf(mx, s);
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  float sum = 0.f;
+  for (int key = lane; key < rs.L; key += 64) {
+    const float p = expf(sc[key] - mx);
+    sc[key] = p;
+    sum += p;
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  __syncthreads();
+  for (int d = lane; d < hd; d += 64) {
+    float acc = 0.f;
+    const float *vr = V + (size_t)d * rs.Lp;
+    for (int key = 0; key < rs.L; ++key) acc = fmaf(sc[key], vr[key], acc);
+    o[(size_t)m * H * hd + head * hd + d] = acc / sum;
+  }
+}
+
+hipError_t launch_attention(const void *q, const void *k_cache, const void *vt_cache, RowSet rs,
+                            int H, int Hkv, int hd, bf16 *o_hi, bf16 *o_lo, float *o_f32,
+                            float *part, int dtype, hipStream_t st) {
+  if (rs.M() <= 0) return hipSuccess;
+  if (dtype == 0) {
+    dim3 grid(rs.M(), H);
+    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), rs.Lp * sizeof(float), st,
+                       (const float *)q, (const float *)k_cache, (const float *)vt_cache, rs, H,
+                       Hkv, hd, 1.0f / sqrtf((float)hd), o_f32);
+    return hipGetLastError();
+  }
+  int splits, chunk;
+  attn_plan(rs, H, Hkv, splits, chunk);
+  const int nqt = attn_tiles(rs, H, Hkv);
+  dim3 grid(nqt, rs.B * Hkv, splits);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
+#define ATTN_CASE(HDV)                                                                          \
+  case HDV:                                                                                     \
+    hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \
+                       (const bf16 *)k_cache, (const bf16 *)vt_cache, rs, H, Hkv, chunk,        \
+                       scale_log2, o_hi, o_lo, part);                                           \
+    if (splits > 1)                                                                             \
+      hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3(rs.B * Hkv * nqt * 32), dim3(64), 0, st,  \
+                         (const float *)part, rs, H, Hkv, nqt, splits, o_hi, o_lo);             \
+    break;
+  switch (hd) {
+    ATTN_CASE(32)
+    ATTN_CASE(64)
+    ATTN_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef ATTN_CASE
+  return hipGetLastError();
+}
+
+}  // namespace dllm

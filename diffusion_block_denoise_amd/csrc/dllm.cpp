@@ -1,0 +1,615 @@
+// Host runtime behind include/dllm.h: configuration checks, workspace plan, the layer sequence
+// of one forward over a row set, the block loop with its cache policy, and the C ABI.
+//
+// Decode (Fast-dLLM v1, block-wise with confidence-threshold parallel decoding and a KV cache
+// refreshed at block boundaries):
+//   prefill       x = [prompt | mask^G]; refresh of block 0
+//   block_begin   full forward over every position of every batch row: all K/V cache slots are
+//                 rewritten and the block rows' statistics serve the block's first step
+//   denoise_step  statistics (kept from the refresh on a block's first step; otherwise a
+//                 forward over the block rows (dual cache), the block and later rows (prefix
+//                 cache) or all rows (no cache)), then the commit on the device
+// Every step of the decode runs in the HIP kernels; the host only sequences launches and reads
+// back the per-row remaining-mask counts (one small copy per step).
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dllm.h"
+#include "kernels.h"
+
+using namespace dllm;
+
+namespace {
+
+std::string g_create_error;
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// ------------------------------------------------------------------------------------------------
+// Validation
+int check_cfg(const dllm_cfg *c, std::string &msg) {
+  auto bad = [&](const char *fmt, ...) {
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    msg = buf;
+    return DLLM_EINVAL;
+  };
+  if (!c) return bad("cfg is NULL");
+  if (c->dtype != DLLM_F32 && c->dtype != DLLM_BF16) return bad("dtype must be DLLM_F32 or DLLM_BF16");
+  if (c->n_layers < 1) return bad("n_layers must be >= 1");
+  if (c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->ffn_dim < 1)
+    return bad("d_model, n_heads, n_kv_heads and ffn_dim must be >= 1");
+  if (c->n_heads % c->n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return bad("head_dim must be 32, 64 or 128");
+  if (c->vocab < 2) return bad("vocab must be >= 2");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return bad("mask_id must be in [0, vocab)");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return bad("rms_eps must be finite and >= 0");
+  if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return bad("rope_base must be finite and > 0");
+  if (!std::isfinite(c->logit_scale)) return bad("logit_scale must be finite");
+  if (c->dtype == DLLM_BF16) {
+    if (c->d_model % 64 || (c->n_heads * c->head_dim) % 64 || c->ffn_dim % 64)
+      return bad("bf16: d_model, n_heads*head_dim and ffn_dim must be multiples of 64");
+  }
+  if (c->batch < 1) return bad("batch must be >= 1");
+  if (c->prompt_len < 0) return bad("prompt_len must be >= 0");
+  if (c->gen_length < 1 || c->block_size < 1) return bad("gen_length and block_size must be >= 1");
+  if (c->block_size > 256) return bad("block_size must be <= 256");
+  if (c->gen_length % c->block_size) return bad("gen_length must be a multiple of block_size");
+  const int nb = c->gen_length / c->block_size;
+  if (c->steps < 0) return bad("steps must be >= 0");
+  const int steps = c->steps ? c->steps : c->gen_length;
+  if (steps % nb) return bad("steps must be a multiple of gen_length/block_size (%d)", nb);
+  if (std::isnan(c->threshold)) return bad("threshold is NaN");
+  if (c->use_cache < 0 || c->use_cache > 2) return bad("use_cache must be 0, 1 or 2");
+  const long long L = (long long)c->prompt_len + c->gen_length;
+  if (L * c->batch > (1LL << 26)) return bad("batch * (prompt_len + gen_length) too large");
+  if (c->dtype == DLLM_F32 && L > 32768) return bad("f32: prompt_len + gen_length must be <= 32768");
+  if ((long long)c->vocab * c->d_model >= (1LL << 40)) return bad("vocab * d_model too large");
+  return DLLM_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Workspace plan
+struct Plan {
+  int B, P, G, Bs, L, Lp, NB, spb, d, H, Hkv, hd, F, V, nq, nkv, dt;
+  size_t esz;  // storage bytes per element (4 or 2)
+  size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
+      off_q, off_apart, off_gpart, off_cnt, off_hpart, off_tok, off_conf, off_p2, off_com,
+      off_ncom, off_rem, total;
+  size_t kv_layer_elems;  // K (or V) elements per layer
+  int n_vtiles, max_tiles;
+};
+
+RowSet rows_of(const Plan &p, int start, int nR) {
+  RowSet r;
+  r.B = p.B; r.L = p.L; r.Lp = p.Lp; r.start = start; r.nR = nR;
+  return r;
+}
+
+void make_plan(const dllm_cfg *c, Plan &p) {
+  p.B = c->batch; p.P = c->prompt_len; p.G = c->gen_length; p.Bs = c->block_size;
+  p.L = p.P + p.G; p.Lp = (p.L + 31) / 32 * 32; p.NB = p.G / p.Bs;
+  const int steps = c->steps ? c->steps : p.G;
+  p.spb = steps / p.NB;
+  p.d = c->d_model; p.H = c->n_heads; p.Hkv = c->n_kv_heads; p.hd = c->head_dim;
+  p.F = c->ffn_dim; p.V = c->vocab; p.nq = p.H * p.hd; p.nkv = p.Hkv * p.hd;
+  p.dt = c->dtype == DLLM_BF16 ? 1 : 0;
+  p.esz = p.dt ? 2 : 4;
+  const size_t Mmax = (size_t)p.B * p.L;
+  const int wa = std::max(p.d, p.nq);
+  p.kv_layer_elems = (size_t)p.B * p.Hkv * p.Lp * p.hd;
+
+  // Row counts that a forward can have: refresh / no cache (B*L), dual step (B*Bs), prefix
+  // step of block b (B*(L - s_b)).
+  std::vector<int> Ms = {p.B * p.L, p.B * p.Bs};
+  for (int b = 0; b < p.NB; ++b) Ms.push_back(p.B * (p.L - (p.P + b * p.Bs)));
+  size_t gpart = 0, apart = 0;
+  int max_tiles = 1;
+  for (int M : Ms) {
+    const int bn = gemm_bn(M, p.dt);
+    const int ffn_virtual = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
+    const int shapes[4][2] = {{p.nq + 2 * p.nkv, p.d}, {p.d, p.nq}, {ffn_virtual, p.d}, {p.d, p.F}};
+    for (auto &s : shapes) {
+      const int splits = gemm_num_splits(M, s[0], s[1], p.dt);
+      if (splits > 1) {
+        gpart = std::max(gpart, (size_t)splits * M * s[0] * sizeof(float));
+        const int bm = gemm_bm(M, p.dt);
+        max_tiles = std::max(max_tiles, ((M + bm - 1) / bm) * ((s[0] + bn - 1) / bn));
+      }
+    }
+    const int nR = M / p.B;
+    apart = std::max(apart, attention_part_bytes(rows_of(p, 0, nR), p.H, p.Hkv, p.hd, p.dt));
+  }
+  // lm_head over the block rows (and the debug logits GEMM, same shape)
+  {
+    const int M = p.B * p.Bs, bn = gemm_bn(M, p.dt);
+    p.n_vtiles = (p.V + bn - 1) / bn;
+    const int splits = gemm_num_splits(M, p.V, p.d, p.dt);
+    if (splits > 1) {
+      gpart = std::max(gpart, (size_t)splits * M * p.V * sizeof(float));
+      const int bm = gemm_bm(M, p.dt);
+      max_tiles = std::max(max_tiles, ((M + bm - 1) / bm) * p.n_vtiles);
+    }
+  }
+  p.max_tiles = max_tiles;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  p.off_x = take(Mmax * 4);
+  p.off_k = take(p.kv_layer_elems * c->n_layers * p.esz);
+  p.off_v = take(p.kv_layer_elems * c->n_layers * p.esz);
+  p.off_cos = take((size_t)p.L * (p.hd / 2) * 4);
+  p.off_sin = take((size_t)p.L * (p.hd / 2) * 4);
+  p.off_h = take(Mmax * p.d * 4);
+  // GEMM inputs: bf16 hi/lo pairs, or one fp32 array in the hi slot
+  p.off_ahi = take(Mmax * wa * (p.dt ? 2 : 4));
+  p.off_alo = take(p.dt ? Mmax * wa * 2 : 0);
+  p.off_acthi = take(Mmax * p.F * (p.dt ? 2 : 4));
+  p.off_actlo = take(p.dt ? Mmax * p.F * 2 : 0);
+  p.off_q = take(Mmax * p.nq * p.esz);
+  p.off_apart = take(apart);
+  p.off_gpart = take(gpart);
+  p.off_cnt = take((size_t)max_tiles * 4);
+  p.off_hpart = take((size_t)p.B * p.Bs * p.n_vtiles * sizeof(HeadPart));
+  p.off_tok = take((size_t)p.B * p.Bs * 4);
+  p.off_conf = take((size_t)p.B * p.Bs * 4);
+  p.off_p2 = take((size_t)p.B * p.Bs * 4);
+  p.off_com = take((size_t)p.B * p.Bs);
+  p.off_ncom = take((size_t)p.B * 4);
+  p.off_rem = take((size_t)p.B * 4);
+  p.total = o;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+struct dllm_handle {
+  dllm_cfg cfg;
+  Plan p;
+  hipStream_t st;
+  const void *embed, *final_norm, *lm_head;
+  std::vector<const void *> layer;
+  char *ws;
+  // carved buffers
+  int *x;
+  char *kc, *vc;
+  float *cos_t, *sin_t, *h;
+  void *a_hi, *a_lo, *act_hi, *act_lo, *q;
+  float *apart, *gpart;
+  int *cnt;
+  HeadPart *hpart;
+  int *tok;
+  float *conf, *p2;
+  uint8_t *com;
+  int *ncom, *rem;
+  // decode state
+  bool have_tokens = false;
+  int block = -1, j = 0;
+  bool fresh = false;
+  bool any_forward = false;
+  RowSet last_rows{};
+  dllm_stats stats{};
+  std::vector<int> h_rem, h_ncom;
+  std::string err;
+};
+
+namespace {
+
+#define HIPCHK(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) {                                                              \
+      h->err = std::string(#expr) + ": " + hipGetErrorString(e_);                        \
+      return DLLM_EHIP;                                                                  \
+    }                                                                                    \
+  } while (0)
+
+inline const void *LW(dllm_t *h, int l, int j) { return h->layer[(size_t)9 * l + j]; }
+
+void *kv_layer(dllm_t *h, char *base, int l) { return base + (size_t)l * h->p.kv_layer_elems * h->p.esz; }
+
+GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M, int N, int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  if (h->p.dt) {
+    g.a_hi = (const bf16 *)a_hi;
+    g.a_lo = (const bf16 *)a_lo;
+  } else {
+    g.a_f32 = (const float *)a_hi;
+  }
+  g.lda = lda;
+  g.M = M; g.N = N; g.K = K;
+  g.partial = h->gpart;
+  g.counters = h->cnt;
+  g.scale = 1.f;
+  return g;
+}
+
+// One forward over row set rs: embedding, n_layers blocks, hidden states left in h.
+int forward(dllm_t *h, RowSet rs) {
+  const Plan &p = h->p;
+  const dllm_cfg &c = h->cfg;
+  const int M = rs.M();
+  const bool bf = p.dt == 1;
+  bf16 *ahi = (bf16 *)h->a_hi, *alo = (bf16 *)h->a_lo;
+  float *af = (float *)h->a_hi;
+  HIPCHK(launch_embed_norm(h->x, h->embed, LW(h, 0, 0), rs, p.d, c.rms_eps, h->h, bf ? ahi : nullptr,
+                           bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (l > 0)
+      HIPCHK(launch_rmsnorm(h->h, LW(h, l, 0), M, M, 0, 0, p.d, c.rms_eps, bf ? ahi : nullptr,
+                            bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+    // Q, K, V projections; rotary embedding; K/V to the cache slots of rows rs
+    {
+      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.nq + 2 * p.nkv, p.d);
+      g.w[0] = LW(h, l, 1); g.w[1] = LW(h, l, 2); g.w[2] = LW(h, l, 3);
+      g.seg_end[0] = p.nq; g.seg_end[1] = p.nq + p.nkv; g.seg_end[2] = p.nq + 2 * p.nkv;
+      g.epi = EPI_QKV;
+      g.rows = rs; g.n_heads = p.H; g.n_kv_heads = p.Hkv; g.head_dim = p.hd;
+      g.rope_cos = h->cos_t; g.rope_sin = h->sin_t;
+      g.q_out = h->q;
+      g.k_cache = kv_layer(h, h->kc, l);
+      g.vt_cache = kv_layer(h, h->vc, l);
+      HIPCHK(launch_gemm(g, p.dt, h->st));
+    }
+    // attention over all cached positions -> a (input of the output projection)
+    HIPCHK(launch_attention(h->q, kv_layer(h, h->kc, l), kv_layer(h, h->vc, l), rs, p.H, p.Hkv, p.hd,
+                            bf ? ahi : nullptr, bf ? alo : nullptr, bf ? nullptr : af, h->apart, p.dt,
+                            h->st));
+    {
+      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.nq, M, p.d, p.nq);
+      g.w[0] = LW(h, l, 4); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
+      g.epi = EPI_RESID; g.resid = h->h; g.ld_out = p.d;
+      HIPCHK(launch_gemm(g, p.dt, h->st));
+    }
+    HIPCHK(launch_rmsnorm(h->h, LW(h, l, 5), M, M, 0, 0, p.d, c.rms_eps, bf ? ahi : nullptr,
+                          bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+    {
+      const int bn = gemm_bn(M, p.dt);
+      const int nvirt = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
+      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, nvirt, p.d);
+      g.w[0] = LW(h, l, 6); g.w[1] = LW(h, l, 7);
+      g.n_half = p.F;
+      g.epi = EPI_SWIGLU;
+      g.ld_act = p.F;
+      if (bf) { g.act_hi = (bf16 *)h->act_hi; g.act_lo = (bf16 *)h->act_lo; }
+      else g.act_f32 = (float *)h->act_hi;
+      HIPCHK(launch_gemm(g, p.dt, h->st));
+    }
+    {
+      GemmArgs g = gemm_base(h, h->act_hi, h->act_lo, p.F, M, p.d, p.F);
+      g.w[0] = LW(h, l, 8); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
+      g.epi = EPI_RESID; g.resid = h->h; g.ld_out = p.d;
+      HIPCHK(launch_gemm(g, p.dt, h->st));
+    }
+  }
+  h->last_rows = rs;
+  h->any_forward = true;
+  return DLLM_OK;
+}
+
+// Final norm of the block rows of the last forward into a (rows 0..B*Bs-1).
+int final_norm_block(dllm_t *h) {
+  const Plan &p = h->p;
+  const RowSet rs = h->last_rows;
+  const int s = p.P + h->block * p.Bs;
+  const bool bf = p.dt == 1;
+  HIPCHK(launch_rmsnorm(h->h, h->final_norm, p.B * p.Bs, p.Bs, rs.nR, s - rs.start, p.d,
+                        h->cfg.rms_eps, bf ? (bf16 *)h->a_hi : nullptr, bf ? (bf16 *)h->a_lo : nullptr,
+                        bf ? nullptr : (float *)h->a_hi, p.dt, h->st));
+  return DLLM_OK;
+}
+
+// Statistics of the block rows: fused lm_head + per-tile softmax partials, then the merge.
+int head(dllm_t *h) {
+  const Plan &p = h->p;
+  int rc = final_norm_block(h);
+  if (rc) return rc;
+  const int M = p.B * p.Bs;
+  GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
+  g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
+  g.epi = EPI_LMHEAD;
+  g.scale = h->cfg.logit_scale;
+  g.head_part = h->hpart; g.n_vtiles = p.n_vtiles; g.vocab = p.V; g.mask_id = h->cfg.mask_id;
+  HIPCHK(launch_gemm(g, p.dt, h->st));
+  HIPCHK(launch_head_merge(h->hpart, M, p.n_vtiles, h->tok, h->conf, h->p2, h->st));
+  return DLLM_OK;
+}
+
+int refresh(dllm_t *h) {
+  int rc = forward(h, rows_of(h->p, 0, h->p.L));
+  if (rc) return rc;
+  h->stats.full_forwards++;
+  return head(h);
+}
+
+int floor_count(const Plan &p, int j) {
+  const int base = p.Bs / p.spb, extra = p.Bs % p.spb;
+  const int k = base + (j < extra ? 1 : 0);
+  return k < 1 ? 1 : k;
+}
+
+int hist_bin(int n) {
+  if (n <= 3) return n;
+  if (n <= 4) return 3;
+  if (n <= 8) return 4;
+  if (n <= 16) return 5;
+  if (n <= 32) return 6;
+  if (n <= 64) return 7;
+  return 8;
+}
+
+double now_ms() {
+  return std::chrono::duration<double, std::milli>(
+             std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+int do_block_begin(dllm_t *h, int b) {
+  const double t0 = now_ms();
+  h->block = b;
+  h->j = 0;
+  int rc = refresh(h);
+  if (rc) return rc;
+  h->fresh = true;
+  h->stats.ms_refresh += now_ms() - t0;
+  return DLLM_OK;
+}
+
+int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
+  const Plan &p = h->p;
+  const double t0 = now_ms();
+  int rc;
+  if (!h->fresh) {
+    const int s = p.P + h->block * p.Bs;
+    if (h->cfg.use_cache == DLLM_NO_CACHE || h->cfg.refresh_every_step) {
+      rc = refresh(h);
+    } else {
+      const int stop = h->cfg.use_cache == DLLM_DUAL_CACHE ? s + p.Bs : p.L;
+      rc = forward(h, rows_of(p, s, stop - s));
+      if (!rc) {
+        h->stats.cached_forwards++;
+        rc = head(h);
+      }
+    }
+    if (rc) return rc;
+  }
+  h->fresh = false;
+  const int s = p.P + h->block * p.Bs;
+  HIPCHK(launch_commit(h->x, p.L, p.B, s, p.Bs, h->tok, h->conf, h->cfg.threshold, floor_count(p, h->j),
+                       h->cfg.mask_id, h->com, h->ncom, h->rem, h->st));
+  HIPCHK(hipMemcpyAsync(h->h_ncom.data(), h->ncom, p.B * 4, hipMemcpyDeviceToHost, h->st));
+  HIPCHK(hipMemcpyAsync(h->h_rem.data(), h->rem, p.B * 4, hipMemcpyDeviceToHost, h->st));
+  HIPCHK(hipStreamSynchronize(h->st));
+  h->j++;
+  h->stats.steps++;
+  int done = 1;
+  for (int b = 0; b < p.B; ++b) {
+    h->stats.committed += h->h_ncom[b];
+    h->stats.commits_hist[hist_bin(h->h_ncom[b])]++;
+    if (h->h_rem[b]) done = 0;
+    if (n_committed) n_committed[b] = h->h_ncom[b];
+  }
+  if (block_done) *block_done = done;
+  h->stats.ms_step += now_ms() - t0;
+  return DLLM_OK;
+}
+
+}  // namespace
+
+// ================================================================================================
+extern "C" {
+
+int dllm_validate_cfg(const dllm_cfg *cfg) {
+  std::string m;
+  return check_cfg(cfg, m);
+}
+
+int dllm_workspace_bytes(const dllm_cfg *cfg, size_t *bytes) {
+  std::string m;
+  int rc = check_cfg(cfg, m);
+  if (rc) return rc;
+  if (!bytes) return DLLM_EINVAL;
+  Plan p;
+  make_plan(cfg, p);
+  *bytes = p.total;
+  return DLLM_OK;
+}
+
+int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
+                dllm_t **out) {
+  if (!out) { g_create_error = "out is NULL"; return DLLM_EINVAL; }
+  *out = nullptr;
+  std::string m;
+  int rc = check_cfg(cfg, m);
+  if (rc) { g_create_error = m; return rc; }
+  if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->layer) {
+    g_create_error = "weights: NULL pointer";
+    return DLLM_EINVAL;
+  }
+  for (int i = 0; i < 9 * cfg->n_layers; ++i)
+    if (!w->layer[i]) { g_create_error = "weights: NULL layer pointer"; return DLLM_EINVAL; }
+  if (!workspace) { g_create_error = "workspace is NULL"; return DLLM_EINVAL; }
+  if ((uintptr_t)workspace % ALIGN) { g_create_error = "workspace must be 256-byte aligned"; return DLLM_EINVAL; }
+  Plan p;
+  make_plan(cfg, p);
+  if (ws_bytes < p.total) {
+    g_create_error = "workspace too small: need " + std::to_string(p.total) + " bytes";
+    return DLLM_ENOSPACE;
+  }
+  dllm_t *h = new (std::nothrow) dllm_handle();
+  if (!h) { g_create_error = "out of host memory"; return DLLM_EINTERNAL; }
+  h->cfg = *cfg;
+  h->p = p;
+  h->st = (hipStream_t)cfg->stream;
+  h->embed = w->embed; h->final_norm = w->final_norm; h->lm_head = w->lm_head;
+  h->layer.assign(w->layer, w->layer + 9 * cfg->n_layers);
+  char *ws = (char *)workspace;
+  h->ws = ws;
+  h->x = (int *)(ws + p.off_x);
+  h->kc = ws + p.off_k; h->vc = ws + p.off_v;
+  h->cos_t = (float *)(ws + p.off_cos); h->sin_t = (float *)(ws + p.off_sin);
+  h->h = (float *)(ws + p.off_h);
+  h->a_hi = ws + p.off_ahi; h->a_lo = ws + p.off_alo;
+  h->act_hi = ws + p.off_acthi; h->act_lo = ws + p.off_actlo;
+  h->q = ws + p.off_q;
+  h->apart = (float *)(ws + p.off_apart);
+  h->gpart = (float *)(ws + p.off_gpart);
+  h->cnt = (int *)(ws + p.off_cnt);
+  h->hpart = (HeadPart *)(ws + p.off_hpart);
+  h->tok = (int *)(ws + p.off_tok);
+  h->conf = (float *)(ws + p.off_conf); h->p2 = (float *)(ws + p.off_p2);
+  h->com = (uint8_t *)(ws + p.off_com);
+  h->ncom = (int *)(ws + p.off_ncom); h->rem = (int *)(ws + p.off_rem);
+  h->h_rem.assign(p.B, 0);
+  h->h_ncom.assign(p.B, 0);
+  // Zero the K/V cache (its padding slots must hold zeros) and the split-K counters; rotary table.
+  auto fail = [&](hipError_t e, const char *what) {
+    g_create_error = std::string(what) + ": " + hipGetErrorString(e);
+    delete h;
+    return DLLM_EHIP;
+  };
+  hipError_t e;
+  if ((e = launch_fill_u32((uint32_t *)h->kc, 0, (p.off_cos - p.off_k) / 4, h->st)) != hipSuccess)
+    return fail(e, "zero cache");
+  if ((e = launch_fill_u32((uint32_t *)h->cnt, 0, (size_t)p.max_tiles, h->st)) != hipSuccess)
+    return fail(e, "zero counters");
+  if ((e = launch_rope_table(h->cos_t, h->sin_t, p.L, p.hd, cfg->rope_base, h->st)) != hipSuccess)
+    return fail(e, "rope table");
+  if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return fail(e, "synchronize");
+  *out = h;
+  return DLLM_OK;
+}
+
+int dllm_prefill(dllm_t *h, const int32_t *prompt) {
+  if (!h) return DLLM_EINVAL;
+  const Plan &p = h->p;
+  if (!prompt && p.P > 0) { h->err = "prompt is NULL"; return DLLM_EINVAL; }
+  for (size_t i = 0; i < (size_t)p.B * p.P; ++i)
+    if (prompt[i] < 0 || prompt[i] >= p.V) { h->err = "prompt id out of range"; return DLLM_EINVAL; }
+  if (p.P > 0)
+    HIPCHK(hipMemcpy2DAsync(h->x, (size_t)p.L * 4, prompt, (size_t)p.P * 4, (size_t)p.P * 4, p.B,
+                            hipMemcpyHostToDevice, h->st));
+  HIPCHK(launch_init_tokens(h->x, p.B, p.P, p.L, h->cfg.mask_id, h->st));
+  h->have_tokens = true;
+  int rc = do_block_begin(h, 0);
+  if (rc) return rc;
+  HIPCHK(hipStreamSynchronize(h->st));
+  return DLLM_OK;
+}
+
+int dllm_block_begin(dllm_t *h, int32_t block) {
+  if (!h) return DLLM_EINVAL;
+  if (!h->have_tokens) { h->err = "block_begin before prefill or set_tokens"; return DLLM_ESTATE; }
+  if (block < 0 || block >= h->p.NB) { h->err = "block out of range"; return DLLM_EINVAL; }
+  return do_block_begin(h, block);
+}
+
+int dllm_denoise_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
+  if (!h) return DLLM_EINVAL;
+  if (!h->have_tokens || h->block < 0) { h->err = "denoise_step before block_begin"; return DLLM_ESTATE; }
+  return do_step(h, n_committed, block_done);
+}
+
+int dllm_generate(dllm_t *h, const int32_t *prompt, int32_t *out, dllm_stats *stats) {
+  if (!h) return DLLM_EINVAL;
+  h->stats = dllm_stats{};
+  int rc = dllm_prefill(h, prompt);
+  if (rc) return rc;
+  const int max_steps = h->p.G + h->p.NB;
+  int steps = 0;
+  for (int b = 0; b < h->p.NB; ++b) {
+    if (b > 0 && (rc = do_block_begin(h, b))) return rc;
+    int done = 0;
+    while (!done) {
+      if ((rc = do_step(h, nullptr, &done))) return rc;
+      if (++steps > max_steps) { h->err = "step limit exceeded"; return DLLM_EINTERNAL; }
+    }
+  }
+  if (out) {
+    HIPCHK(hipMemcpyAsync(out, h->x, (size_t)h->p.B * h->p.L * 4, hipMemcpyDeviceToHost, h->st));
+    HIPCHK(hipStreamSynchronize(h->st));
+  }
+  if (stats) *stats = h->stats;
+  return DLLM_OK;
+}
+
+int dllm_get_tokens(dllm_t *h, int32_t *x) {
+  if (!h || !x) return DLLM_EINVAL;
+  HIPCHK(hipMemcpyAsync(x, h->x, (size_t)h->p.B * h->p.L * 4, hipMemcpyDeviceToHost, h->st));
+  HIPCHK(hipStreamSynchronize(h->st));
+  return DLLM_OK;
+}
+
+int dllm_set_tokens(dllm_t *h, const int32_t *x) {
+  if (!h || !x) return DLLM_EINVAL;
+  const size_t n = (size_t)h->p.B * h->p.L;
+  for (size_t i = 0; i < n; ++i)
+    if (x[i] < 0 || x[i] >= h->p.V) { h->err = "token id out of range"; return DLLM_EINVAL; }
+  HIPCHK(hipMemcpyAsync(h->x, x, n * 4, hipMemcpyHostToDevice, h->st));
+  HIPCHK(hipStreamSynchronize(h->st));
+  h->have_tokens = true;
+  return DLLM_OK;
+}
+
+int dllm_get_step_info(dllm_t *h, int32_t *tok, float *conf, float *p2, uint8_t *committed) {
+  if (!h) return DLLM_EINVAL;
+  if (!h->any_forward) { h->err = "no forward yet"; return DLLM_ESTATE; }
+  const size_t n = (size_t)h->p.B * h->p.Bs;
+  if (tok) HIPCHK(hipMemcpyAsync(tok, h->tok, n * 4, hipMemcpyDeviceToHost, h->st));
+  if (conf) HIPCHK(hipMemcpyAsync(conf, h->conf, n * 4, hipMemcpyDeviceToHost, h->st));
+  if (p2) HIPCHK(hipMemcpyAsync(p2, h->p2, n * 4, hipMemcpyDeviceToHost, h->st));
+  if (committed) HIPCHK(hipMemcpyAsync(committed, h->com, n, hipMemcpyDeviceToHost, h->st));
+  HIPCHK(hipStreamSynchronize(h->st));
+  return DLLM_OK;
+}
+
+int dllm_debug_block_logits(dllm_t *h, float *logits_dev) {
+  if (!h || !logits_dev) return DLLM_EINVAL;
+  if (!h->any_forward) { h->err = "no forward yet"; return DLLM_ESTATE; }
+  const Plan &p = h->p;
+  int rc = final_norm_block(h);
+  if (rc) return rc;
+  const int M = p.B * p.Bs;
+  GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
+  g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
+  g.epi = EPI_STORE; g.out_f32 = logits_dev; g.ld_out = p.V; g.scale = h->cfg.logit_scale;
+  HIPCHK(launch_gemm(g, p.dt, h->st));
+  HIPCHK(launch_mask_column(logits_dev, M, p.V, h->cfg.mask_id, h->st));
+  HIPCHK(hipStreamSynchronize(h->st));
+  return DLLM_OK;
+}
+
+int dllm_get_stats(dllm_t *h, dllm_stats *stats) {
+  if (!h || !stats) return DLLM_EINVAL;
+  *stats = h->stats;
+  return DLLM_OK;
+}
+
+int dllm_get_position(dllm_t *h, int32_t *block, int32_t *step) {
+  if (!h) return DLLM_EINVAL;
+  if (block) *block = h->block;
+  if (step) *step = h->j;
+  return DLLM_OK;
+}
+
+const char *dllm_last_error(const dllm_t *h) {
+  return h ? h->err.c_str() : g_create_error.c_str();
+}
+
+void dllm_destroy(dllm_t *h) { delete h; }
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Internal interface between the host runtime (dllm.cpp) and the gfx950 kernels.
+// Every launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace dllm {
+
+typedef __hip_bfloat16 bf16;
+
+// Rows that one forward processes: for each batch row b, positions [start, start + nR).
+// Row m of every activation buffer is (b = m / nR, position = start + m % nR).
+struct RowSet {
+  int B;      // batch rows
+  int L;      // sequence length (positions per batch row)
+  int Lp;     // cache slots per batch row and head: L rounded up to a multiple of 32
+  int start;  // first position
+  int nR;     // positions per batch row
+  int M() const { return B * nR; }
+};
+
+// GEMM epilogues.  The GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (fp32 accumulate).
+enum Epi : int {
+  EPI_STORE = 0,   // out_f32[m*ld_out + n] = scale * C
+  EPI_RESID = 1,   // resid[m*ld_out + n] += C
+  EPI_QKV = 2,     // rotary embedding of q and k, q to q_out, k and v to the cache slots
+  EPI_SWIGLU = 3,  // tiles hold gate and up halves: act[m][f] = silu(g) * u
+  EPI_LMHEAD = 4,  // per row and vocab tile: max, argmax, runner-up max, sum of exp
+};
+
+// Per-(row, vocab tile) softmax partial of the fused lm_head.
+struct HeadPart {
+  float m1;   // max scaled logit in the tile
+  int idx;    // its vocab id (lowest among equal maxima)
+  float m2;   // best scaled logit among the tile's other ids
+  float z;    // sum over the tile of exp(logit - m1)
+};
+
+struct GemmArgs {
+  // A operand: M x K, row-major with leading dimension lda.
+  //   bf16 path: a_hi + a_lo (two bf16 arrays whose sum is the fp32 activation)
+  //   f32 path : a_f32
+  const bf16 *a_hi, *a_lo;
+  const float *a_f32;
+  int lda;
+  // W operand: N x K rows from up to three segments (torch Linear layout, ld = K).
+  // Plain mode: virtual row n lives in segment s with seg_end[s-1] <= n < seg_end[s].
+  // SwiGLU mode: tile t, column c < BN/2 -> gate row t*BN/2 + c; else up row t*BN/2 + c - BN/2,
+  //   rows >= n_half (ffn_dim) are zero.
+  const void *w[3];
+  int seg_end[3];
+  int n_half;     // SwiGLU: ffn_dim
+  int M, N, K;    // N is the virtual width (SwiGLU: 2 * ceil(ffn_dim / (BN/2)) * (BN/2))
+  int k_split;    // K elements per split (multiple of the kernel's BK); gridDim.z splits
+  float *partial; // split-K partial tiles [splits][M][N] fp32 (when gridDim.z > 1)
+  int *counters;  // per-tile arrival counters (zero between launches)
+  int epi;
+  // epilogue operands
+  float *out_f32; int ld_out; float scale;        // STORE
+  float *resid;                                   // RESID (ld_out)
+  // QKV
+  RowSet rows; int n_heads, n_kv_heads, head_dim;
+  const float *rope_cos, *rope_sin;               // [L][head_dim/2]
+  void *q_out;                                    // [M][n_heads*head_dim] in storage type
+  void *k_cache, *vt_cache;                       // this layer: [B][Hkv][Lp][hd] and [B][Hkv][hd][Lp]
+  // SWIGLU output (bf16 path: hi/lo; f32 path: f32), ld = ld_act
+  bf16 *act_hi, *act_lo; float *act_f32; int ld_act;
+  // LMHEAD
+  HeadPart *head_part; int n_vtiles; int vocab; int mask_id;
+};
+
+// Storage-type tag for templates: 0 = f32, 1 = bf16.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t st);
+// Tile width (N direction) that launch_gemm uses for a given M and dtype; SwiGLU and
+// the lm_head partial layout depend on it.
+int gemm_bn(int M, int dtype);
+int gemm_bm(int M, int dtype);
+int gemm_num_splits(int M, int N, int K, int dtype);
+
+// h[m] = embed[x[b][p]] (fp32); a = rmsnorm(h) * g written as hi/lo (bf16) or f32.
+hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rows, int d,
+                             float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
+                             hipStream_t st);
+// a[i] = rmsnorm(h[row_of(i)]) * g for n rows; row_of(i) = (i / per) * stride + off + i % per.
+hipError_t launch_rmsnorm(const float *h, const void *gain, int n, int per, int stride, int off,
+                          int d, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
+                          hipStream_t st);
+// Non-causal attention of the rows' queries over all L cached positions.
+hipError_t launch_attention(const void *q, const void *k_cache, const void *vt_cache, RowSet rows,
+                            int n_heads, int n_kv_heads, int head_dim, bf16 *o_hi, bf16 *o_lo,
+                            float *o_f32, float *part, int dtype, hipStream_t st);
+size_t attention_part_bytes(RowSet rows, int n_heads, int n_kv_heads, int head_dim, int dtype);
+// Merge lm_head partials: tok, conf = 1/Z, p2 = exp(m2 - m1)/Z per row.
+hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,
+                             float *p2, hipStream_t st);
+// Commit for each batch row over its block [s, s+Bs).
+hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
+                         float threshold, int k_floor, int mask_id, uint8_t *committed,
+                         int *n_committed, int *remaining, hipStream_t st);
+// x[b][p] = mask_id for P <= p < L (the prompt part is left as it is).
+hipError_t launch_init_tokens(int *x, int B, int P, int L, int mask_id, hipStream_t st);
+// cos/sin tables [L][hd/2] of theta = p * base^(-2i/hd), computed in fp64 on the device.
+hipError_t launch_rope_table(float *cos_t, float *sin_t, int L, int hd, float base, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t st);
+// Mark the mask id column (-inf) of debug logits rows.
+hipError_t launch_mask_column(float *logits, int n_rows, int vocab, int mask_id, hipStream_t st);
+
+}  // namespace dllm

@@ -1,0 +1,261 @@
+// Row-wise and bookkeeping kernels: embedding gather fused with RMSNorm, RMSNorm, the merge of
+// the fused lm_head's per-tile softmax partials, the commit rule, token-state initialisation,
+// the rotary table, and fills.
+#include "kernels.h"
+
+#include <limits.h>
+
+namespace dllm {
+
+template <typename T> __device__ inline float ld_f(const T *p, size_t i);
+template <> __device__ inline float ld_f<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ inline float ld_f<bf16>(const bf16 *p, size_t i) { return __bfloat162float(p[i]); }
+
+__device__ inline float block_sum(float v) {
+  __shared__ float red[4];
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  const int nw = blockDim.x / 64;
+  for (int w = 0; w < nw; ++w) s += red[w];
+  return s;
+}
+
+// One 256-thread workgroup per row: a = h * rsqrt(mean(h^2) + eps) * g.
+template <typename T>
+__device__ void norm_row(const float *hr, const T *gain, int d, float eps, size_t out_off,
+                         bf16 *a_hi, bf16 *a_lo, float *a_f32) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += hr[i] * hr[i];
+  ss = block_sum(ss);
+  const float r = rsqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float v = hr[i] * r * ld_f<T>(gain, i);
+    if (a_f32) {
+      a_f32[out_off + i] = v;
+    } else {
+      const bf16 hi = __float2bfloat16(v);
+      a_hi[out_off + i] = hi;
+      a_lo[out_off + i] = __float2bfloat16(v - __bfloat162float(hi));
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int *x, const T *embed,
+                                                         const T *gain, RowSet rs, int d, float eps,
+                                                         float *h, bf16 *a_hi, bf16 *a_lo,
+                                                         float *a_f32) {
+  const int m = blockIdx.x;
+  const int b = m / rs.nR, p = rs.start + m % rs.nR;
+  const int tok = x[(size_t)b * rs.L + p];
+  float *hr = h + (size_t)m * d;
+  const T *er = embed + (size_t)tok * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) hr[i] = ld_f<T>(er, i);
+  __syncthreads();
+  norm_row<T>(hr, gain, d, eps, (size_t)m * d, a_hi, a_lo, a_f32);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *h, const T *gain, int per,
+                                                      int stride, int off, int d, float eps,
+                                                      bf16 *a_hi, bf16 *a_lo, float *a_f32) {
+  const int i = blockIdx.x;
+  const int row = (i / per) * stride + off + i % per;
+  norm_row<T>(h + (size_t)row * d, gain, d, eps, (size_t)i * d, a_hi, a_lo, a_f32);
+}
+
+hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rs, int d,
+                             float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
+                             hipStream_t st) {
+  if (rs.M() <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(rs.M()), dim3(256), 0, st, x,
+                       (const float *)embed, (const float *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
+  else
+    hipLaunchKernelGGL(embed_norm_kernel<bf16>, dim3(rs.M()), dim3(256), 0, st, x,
+                       (const bf16 *)embed, (const bf16 *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float *h, const void *gain, int n, int per, int stride, int off,
+                          int d, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
+                          hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(n), dim3(256), 0, st, h, (const float *)gain,
+                       per, stride, off, d, eps, a_hi, a_lo, a_f32);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(n), dim3(256), 0, st, h, (const bf16 *)gain, per,
+                       stride, off, d, eps, a_hi, a_lo, a_f32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// lm_head partial merge.  One wave per row; lane j folds tiles j, j+64, ... in order, then a
+// fixed butterfly combines the lanes, so the result does not depend on scheduling.
+struct Part4 {
+  float m1; int idx; float m2; float z;
+};
+__device__ inline Part4 part_merge(Part4 a, Part4 b) {
+  const bool bw = (b.m1 > a.m1) || (b.m1 == a.m1 && b.idx < a.idx);
+  const Part4 w = bw ? b : a, l = bw ? a : b;
+  Part4 r;
+  r.m1 = w.m1;
+  r.idx = w.idx;
+  r.m2 = fmaxf(w.m2, l.m1);
+  r.z = w.z + (l.m1 == -INFINITY ? 0.f : l.z * __expf(l.m1 - w.m1));
+  return r;
+}
+
+__global__ __launch_bounds__(64) void head_merge_kernel(const HeadPart *part, int n_vtiles,
+                                                        int *tok, float *conf, float *p2) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  Part4 acc = {-INFINITY, INT_MAX, -INFINITY, 0.f};
+  const HeadPart *pr = part + (size_t)row * n_vtiles;
+  for (int t = lane; t < n_vtiles; t += 64) {
+    const HeadPart hp = pr[t];
+    Part4 x = {hp.m1, hp.idx, hp.m2, hp.z};
+    acc = part_merge(acc, x);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    Part4 o;
+    o.m1 = __shfl_xor(acc.m1, off, 64);
+    o.idx = __shfl_xor(acc.idx, off, 64);
+    o.m2 = __shfl_xor(acc.m2, off, 64);
+    o.z = __shfl_xor(acc.z, off, 64);
+    // both partners must compute the same value: order the operands by lane
+    acc = (lane & off) ? part_merge(o, acc) : part_merge(acc, o);
+  }
+  if (lane == 0) {
+    if (acc.idx == INT_MAX) {
+      // no finite logit in the row (NaN input): token 0, confidence NaN (ranks last)
+      tok[row] = 0;
+      conf[row] = __int_as_float(0x7fc00000);
+      p2[row] = 0.f;
+    } else {
+      tok[row] = acc.idx;
+      conf[row] = 1.0f / acc.z;
+      p2[row] = (acc.m2 == -INFINITY ? 0.f : __expf(acc.m2 - acc.m1)) / acc.z;
+    }
+  }
+}
+
+hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,
+                             float *p2, hipStream_t st) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(head_merge_kernel, dim3(n_rows), dim3(64), 0, st, part, n_vtiles, tok, conf,
+                     p2);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Commit: one workgroup per batch row, thread i owns block position s + i.  A masked position
+// commits when conf > threshold or when fewer than k_floor masked positions rank above it
+// (confidence descending, then position ascending; NaN ranks last).
+__global__ __launch_bounds__(256) void commit_kernel(int *x, int L, int s, int Bs, const int *tok,
+                                                     const float *conf, float threshold,
+                                                     int k_floor, int mask_id, uint8_t *committed,
+                                                     int *n_committed, int *remaining) {
+  __shared__ float cs[256];
+  __shared__ int ms[256];
+  __shared__ int cnt[2];
+  const int b = blockIdx.x, i = threadIdx.x;
+  if (i < 2) cnt[i] = 0;
+  int masked = 0;
+  float c = -INFINITY;
+  if (i < Bs) {
+    masked = x[(size_t)b * L + s + i] == mask_id;
+    c = conf[(size_t)b * Bs + i];
+    if (c != c) c = -INFINITY;
+    cs[i] = c;
+    ms[i] = masked;
+  }
+  __syncthreads();
+  int commit = 0;
+  if (i < Bs && masked) {
+    int rank = 0;
+    for (int j = 0; j < Bs; ++j)
+      rank += ms[j] && (cs[j] > c || (cs[j] == c && j < i));
+    commit = (c > threshold) || (rank < k_floor);
+    if (commit) x[(size_t)b * L + s + i] = tok[(size_t)b * Bs + i];
+  }
+  if (i < Bs) committed[(size_t)b * Bs + i] = (uint8_t)commit;
+  if (commit) atomicAdd(&cnt[0], 1);
+  if (masked && !commit) atomicAdd(&cnt[1], 1);
+  __syncthreads();
+  if (i == 0) {
+    n_committed[b] = cnt[0];
+    remaining[b] = cnt[1];
+  }
+}
+
+hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
+                         float threshold, int k_floor, int mask_id, uint8_t *committed,
+                         int *n_committed, int *remaining, hipStream_t st) {
+  if (Bs > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(256), 0, st, x, L, s, Bs, tok, conf, threshold,
+                     k_floor, mask_id, committed, n_committed, remaining);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+__global__ void init_tokens_kernel(int *x, int B, int P, int L, int mask_id) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)B * L) return;
+  if ((int)(i % L) >= P) x[i] = mask_id;
+}
+
+hipError_t launch_init_tokens(int *x, int B, int P, int L, int mask_id, hipStream_t st) {
+  const size_t n = (size_t)B * L;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(init_tokens_kernel, dim3((n + 255) / 256), dim3(256), 0, st, x, B, P, L,
+                     mask_id);
+  return hipGetLastError();
+}
+
+__global__ void rope_table_kernel(float *cos_t, float *sin_t, int L, int hd, double base) {
+  const int half = hd / 2;
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)L * half) return;
+  const int p = i / half, j = i % half;
+  const double theta = (double)p * pow(base, -2.0 * j / (double)hd);
+  cos_t[i] = (float)cos(theta);
+  sin_t[i] = (float)sin(theta);
+}
+
+hipError_t launch_rope_table(float *cos_t, float *sin_t, int L, int hd, float base, hipStream_t st) {
+  const size_t n = (size_t)L * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, cos_t, sin_t, L, hd,
+                     (double)base);
+  return hipGetLastError();
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t v, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+__global__ void mask_column_kernel(float *logits, int n_rows, int vocab, int mask_id) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < n_rows) logits[(size_t)r * vocab + mask_id] = -INFINITY;
+}
+
+hipError_t launch_mask_column(float *logits, int n_rows, int vocab, int mask_id, hipStream_t st) {
+  hipLaunchKernelGGL(mask_column_kernel, dim3((n_rows + 63) / 64), dim3(64), 0, st, logits, n_rows,
+                     vocab, mask_id);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

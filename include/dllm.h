@@ -1,0 +1,218 @@
+/*
+ * dllm.h: C ABI of the MI355X (gfx950) library for cached block-wise
+ * masked-diffusion LLM decoding.
+ *
+ * The method (Fast-dLLM v1, training-free): the generated region is split into
+ * blocks that are denoised left to right; in each step every still-masked
+ * position of the current block gets the softmax of the model's logits, and
+ * every position whose top probability clears the threshold is committed at
+ * once, never to be revised; K/V of positions outside the recomputed rows are
+ * reused from a cache that is refreshed only when a block starts.
+ *   - Fast-dLLM README, track table ("KV Cache + Parallel Decoding") and Quick
+ *     Start (knobs --gen_length --steps --block_size; Dream command
+ *     alg=confidence_threshold, threshold=0.9, use_cache=true).
+ *   - "Fast-dLLM: Four Acceleration Tracks ...", sections "The v1 Mechanism"
+ *     and "Fast-dLLM v1 Versus a Standard Diffusion Sampler".
+ *   - Streaming-dLLM README, throughput tables: "Prefix-Cache" and
+ *     "Fast-dLLM" columns against the no-cache backbones.
+ *
+ * Conventions for every function below
+ *   - Return 0 on success or a negative DLLM_E* code; dllm_last_error() gives
+ *     a message.  No C++ exception crosses this boundary.
+ *   - Device pointers are HIP device addresses on the current device; "host"
+ *     arguments are ordinary host memory.
+ *   - All device work is enqueued on cfg.stream (a hipStream_t; NULL = the
+ *     null stream).  Calls that read or write host arrays synchronise that
+ *     stream before returning; dllm_block_begin does not.
+ *   - One host thread at a time per handle.  Several handles may share the
+ *     same weights read-only.
+ *   - The library allocates no device memory: the caller passes the weights
+ *     and one workspace of dllm_workspace_bytes() bytes, owns both, and must
+ *     keep both alive until dllm_destroy.  The handle owns host state only.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define DLLM_OK 0
+#define DLLM_EINVAL -1     /* bad argument or configuration */
+#define DLLM_ENOSPACE -2   /* workspace smaller than dllm_workspace_bytes() */
+#define DLLM_ESTATE -3     /* call out of order (e.g. a step before prefill) */
+#define DLLM_EHIP -4       /* a HIP runtime call failed; the message names it */
+#define DLLM_EINTERNAL -5  /* unexpected internal failure */
+
+/* Storage type of weights and KV cache. */
+#define DLLM_F32 0
+#define DLLM_BF16 1
+
+/* Cache policy (use_cache). */
+#define DLLM_NO_CACHE 0     /* every step is a full forward                      */
+#define DLLM_PREFIX_CACHE 1 /* steps recompute the block and every later row      */
+#define DLLM_DUAL_CACHE 2   /* steps recompute the block rows only                */
+
+/*
+ * Model shape and decode knobs.
+ *   Shape: an LLaDA/Dream-style bidirectional transformer (Fast-dLLM README
+ *   track table, backbones Dream and LLaDA): pre-norm RMSNorm, rotary positions
+ *   (rotate-half form), attention with n_heads query heads over n_kv_heads K/V
+ *   heads (n_heads % n_kv_heads == 0), SwiGLU feed-forward, untied embedding
+ *   and lm_head, no biases.  Constraints: head_dim in {32, 64, 128}; for
+ *   DLLM_BF16, d_model, n_heads*head_dim and ffn_dim are multiples of 64.
+ *   mask_id < vocab is the mask token; it is excluded from every softmax.
+ *   logit_scale multiplies the lm_head output before the softmax.
+ *   Knobs (Fast-dLLM README, Quick Start): gen_length is a multiple of
+ *   block_size; steps (0 = gen_length) is the diffusion step budget, a multiple
+ *   of gen_length/block_size, and sets the per-step commit floor (the block's
+ *   positions spread evenly over its steps/n_blocks steps; 1 per step by
+ *   default); threshold: a masked position commits when its confidence (top
+ *   softmax probability) is strictly greater; use_cache: DLLM_*_CACHE.
+ *   block_size <= 256.  refresh_every_step != 0 refreshes the whole cache at
+ *   every step (a test hook: it must reproduce no-cache decoding).
+ *   All batch rows share prompt_len and advance block by block together.
+ */
+typedef struct dllm_cfg {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab, mask_id;
+  float rms_eps, rope_base, logit_scale;
+  int32_t dtype; /* DLLM_F32 | DLLM_BF16 */
+  int32_t batch, prompt_len, gen_length, block_size;
+  int32_t steps;
+  float threshold;
+  int32_t use_cache;
+  int32_t refresh_every_step;
+  void *stream; /* hipStream_t */
+} dllm_cfg;
+
+/*
+ * Device pointers to the weights, in cfg.dtype, torch Linear layout
+ * [out_features, in_features], row-major, contiguous:
+ *   embed [vocab, d_model], final_norm [d_model], lm_head [vocab, d_model];
+ *   layer[9*l + j] for layer l, j in order:
+ *     0 attn_norm [d_model]            1 wq [n_heads*head_dim, d_model]
+ *     2 wk [n_kv_heads*head_dim, d_model]  3 wv [n_kv_heads*head_dim, d_model]
+ *     4 wo [d_model, n_heads*head_dim]  5 ffn_norm [d_model]
+ *     6 w_gate [ffn_dim, d_model]       7 w_up [ffn_dim, d_model]
+ *     8 w_down [d_model, ffn_dim]
+ * Device pointers must be 16-byte aligned.  The array `layer` itself is host
+ * memory and is copied by dllm_create.
+ */
+typedef struct dllm_weights {
+  const void *embed, *final_norm, *lm_head;
+  const void *const *layer; /* host array of 9*n_layers device pointers */
+} dllm_weights;
+
+/* Counters of a handle since dllm_create (or the last dllm_prefill). */
+typedef struct dllm_stats {
+  int64_t steps;            /* denoising steps taken                         */
+  int64_t full_forwards;    /* refresh / no-cache forwards                   */
+  int64_t cached_forwards;  /* cached-step forwards                          */
+  int64_t committed;        /* tokens committed (all batch rows)             */
+  int64_t commits_hist[9];  /* steps by tokens committed per row per step:
+                               [0]=0, [1]=1, [2]=2, [3]=3-4, [4]=5-8, [5]=9-16,
+                               [6]=17-32, [7]=33-64, [8]=65+                 */
+  double ms_refresh;        /* host wall time in block refreshes (ms)        */
+  double ms_step;           /* host wall time in denoise steps (ms)          */
+} dllm_stats;
+
+typedef struct dllm_handle dllm_t;
+
+/* Check a configuration without touching the GPU.  Host only. */
+int dllm_validate_cfg(const dllm_cfg *cfg);
+
+/* Workspace bytes that a handle for cfg needs.  Host only.  EINVAL for a bad cfg. */
+int dllm_workspace_bytes(const dllm_cfg *cfg, size_t *bytes);
+
+/*
+ * Create a handle.  `workspace` is caller-owned device memory of ws_bytes
+ * (>= dllm_workspace_bytes, 256-byte aligned); it holds the token state, the
+ * KV cache (n_layers x batch x n_kv_heads x (prompt_len+gen_length) x head_dim
+ * for K and V) and all intermediate buffers.  Initialises the workspace on
+ * cfg.stream and synchronises it.
+ */
+int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
+                dllm_t **out);
+
+/*
+ * x = [prompt | mask_id x gen_length] for every batch row, then the refresh of
+ * block 0 (full forward over all positions, every cache slot written; its
+ * block-row statistics serve the block's first step).  prompt: host int32
+ * [batch, prompt_len], ids in [0, vocab).  Synchronises.
+ */
+int dllm_prefill(dllm_t *h, const int32_t *prompt);
+
+/*
+ * Block-boundary refresh (Fast-dLLM v1: the cache is refreshed when a block
+ * starts): full forward of all rows of every batch row on the current token
+ * state; all K/V cache slots are rewritten; the block's first-step statistics
+ * are kept for the next dllm_denoise_step.  0 <= block < gen_length/block_size.
+ * Asynchronous.  ESTATE before dllm_prefill or dllm_set_tokens.
+ */
+int dllm_block_begin(dllm_t *h, int32_t block);
+
+/*
+ * One denoising step of the current block: the statistics (from the refresh on
+ * the block's first step, otherwise from a cached forward: block rows for the
+ * dual cache, block and later rows for the prefix cache, all rows with no
+ * cache), then the commit: in every batch row, each masked block position
+ * with confidence > threshold, plus at least the floor's number of most
+ * confident ones (ties: lower position), gets its argmax token.
+ * n_committed: host int32 [batch] or NULL; block_done: host int32 or NULL,
+ * set to 1 when no batch row has a masked position left in the block.
+ * Synchronises (one small device-to-host copy).
+ */
+int dllm_denoise_step(dllm_t *h, int32_t *n_committed, int32_t *block_done);
+
+/*
+ * Whole decode: prefill, then every block in order (block_begin for b > 0,
+ * steps until the block is done).  out: host int32 [batch, prompt_len +
+ * gen_length] or NULL; stats: host or NULL (counters of this call).
+ */
+int dllm_generate(dllm_t *h, const int32_t *prompt, int32_t *out, dllm_stats *stats);
+
+/* Token state [batch, prompt_len + gen_length] to host.  Synchronises. */
+int dllm_get_tokens(dllm_t *h, int32_t *x);
+
+/*
+ * Overwrite the token state from host (teacher forcing, resume).  The cache
+ * and the current block are left as they are; call dllm_block_begin to
+ * refresh the cache from the new state.  Ids must be in [0, vocab).
+ */
+int dllm_set_tokens(dllm_t *h, const int32_t *x);
+
+/*
+ * Statistics of the last step's forward and its commit, host arrays
+ * [batch, block_size] each (any may be NULL): argmax token, confidence (top
+ * probability), runner-up probability, and 1 where the position was committed
+ * by that step.  Synchronises.
+ */
+int dllm_get_step_info(dllm_t *h, int32_t *tok, float *conf, float *p2, uint8_t *committed);
+
+/*
+ * Test aid, never used by the decode: write the scaled logits of the block rows
+ * of the last forward (mask id = -inf) to a caller-owned DEVICE buffer of
+ * batch*block_size*vocab floats, row-major.  Synchronises.
+ */
+int dllm_debug_block_logits(dllm_t *h, float *logits_dev);
+
+/* Counters since dllm_create (dllm_generate resets them at its start). */
+int dllm_get_stats(dllm_t *h, dllm_stats *stats);
+
+/* Device-side phase of the handle for tests: current block, step index in it. */
+int dllm_get_position(dllm_t *h, int32_t *block, int32_t *step);
+
+/* Message of the last error on h (or of the last failed dllm_create when h is NULL). */
+const char *dllm_last_error(const dllm_t *h);
+
+/* Free the handle's host state.  Does not touch the weights or the workspace. */
+void dllm_destroy(dllm_t *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

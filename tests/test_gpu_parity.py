@@ -1,0 +1,168 @@
+"""GPU library against the oracle, through the C ABI (teacher-forced per step, and free-running
+invariants).  Needs an MI355X and a built libdllm.so."""
+
+import numpy as np
+import pytest
+
+import synth
+from parity import Report, assert_report, oracle_decoder, teacher_forced_block
+
+pytestmark = pytest.mark.gpu
+
+
+def _handle(cfg, **kw):
+    import torch
+    from diffusion_block_denoise_amd import dllm
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    W = synth.weights_torch(cfg, device="cuda")
+    return dllm.Handle(cfg, W, **kw)
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def small_bf16(**kw):
+    base = dict(n_layers=2, d_model=256, n_heads=8, n_kv_heads=2, head_dim=32, ffn_dim=512,
+                vocab=1000, mask_id=999, batch=2, prompt_len=40, gen_length=32, block_size=16,
+                use_cache=2, random_gains=True)
+    base.update(kw)
+    return synth.configs.get("small_bf16", **base)
+
+
+# ------------------------------------------------------------------------------ fp32 tiny model
+def test_tiny_f32_generate_exact_sequence():
+    cfg = synth.configs.get("tiny_f32")
+    _log("case tiny_f32 generate")
+    h = _handle(cfg)
+    x_gpu, st = h.generate(synth.prompt_np(cfg))
+    dec = oracle_decoder(cfg, keep_logits=False)
+    x_ref, recs = dec.generate(synth.prompt_np(cfg))
+    assert np.array_equal(x_gpu, x_ref)
+    assert st["steps"] == len(recs)
+    assert st["full_forwards"] == cfg["gen_length"] // cfg["block_size"]
+
+
+def test_tiny_f32_teacher_forced_all_blocks():
+    cfg = synth.configs.get("tiny_f32", random_gains=True)
+    _log("case tiny_f32 teacher-forced")
+    h = _handle(cfg)
+    dec = oracle_decoder(cfg)
+    rep = Report()
+    for b in range(cfg["gen_length"] // cfg["block_size"]):
+        teacher_forced_block(cfg, h, dec, synth.block_state_np(cfg, b), b, rep)
+    _log(rep)
+    assert_report(cfg, rep)
+
+
+# ------------------------------------------------------------------------------ bf16
+@pytest.mark.parametrize("variant", [
+    dict(),                                                  # GQA 8/2, hd 32, dual, batch 2
+    dict(use_cache=1, n_kv_heads=4, head_dim=64, n_heads=4),  # prefix cache, hd 64, MHA
+    dict(use_cache=0, head_dim=128, n_heads=2, n_kv_heads=1, batch=1),  # no cache, hd 128
+    dict(batch=5, block_size=32, gen_length=64, prompt_len=17),  # M = 160 rows, ragged L
+    dict(block_size=64, gen_length=64, batch=1, threshold=0.5),  # 64-wide block
+])
+def test_bf16_teacher_forced(variant):
+    cfg = small_bf16(**variant)
+    _log("case bf16 teacher-forced", variant)
+    h = _handle(cfg)
+    dec = oracle_decoder(cfg)
+    rep = Report()
+    for b in range(cfg["gen_length"] // cfg["block_size"]):
+        teacher_forced_block(cfg, h, dec, synth.block_state_np(cfg, b), b, rep)
+    _log(rep)
+    assert_report(cfg, rep)
+
+
+def test_small_bf16_workload_teacher_forced():
+    """The 8-layer d=1024 vocab-32000 workload, prefix-only cache, blocks 0, 3 and 7."""
+    cfg = synth.configs.get("small_bf16")
+    _log("case small_bf16 workload")
+    h = _handle(cfg)
+    dec = oracle_decoder(cfg)
+    rep = Report()
+    for b in (0, 3, 7):
+        teacher_forced_block(cfg, h, dec, synth.block_state_np(cfg, b), b, rep)
+        _log("block", b, rep)
+    assert_report(cfg, rep)
+
+
+# ------------------------------------------------------------------------------ invariants
+def test_threshold_above_one_commits_one_per_step():
+    cfg = small_bf16(threshold=1.5)
+    h = _handle(cfg)
+    x, st = h.generate(synth.prompt_np(cfg))
+    assert st["steps"] == cfg["gen_length"]
+    assert st["commits_hist"][1] == cfg["gen_length"] * cfg["batch"]
+    assert (x[:, cfg["prompt_len"]:] != cfg["mask_id"]).all()
+
+
+def test_threshold_zero_commits_whole_block():
+    cfg = small_bf16(threshold=0.0)
+    h = _handle(cfg)
+    x, st = h.generate(synth.prompt_np(cfg))
+    nb = cfg["gen_length"] // cfg["block_size"]
+    assert st["steps"] == nb and st["cached_forwards"] == 0
+    assert st["committed"] == cfg["gen_length"] * cfg["batch"]
+
+
+def test_refresh_every_step_equals_no_cache():
+    cfg2 = small_bf16(use_cache=2, threshold=0.9)
+    cfg0 = small_bf16(use_cache=0, threshold=0.9)
+    xa, sa = _handle(cfg2, refresh_every_step=True).generate(synth.prompt_np(cfg2))
+    xb, sb = _handle(cfg0).generate(synth.prompt_np(cfg0))
+    assert np.array_equal(xa, xb)
+    assert sa["steps"] == sb["steps"]
+
+
+def test_commits_are_never_revised_and_write_argmax():
+    cfg = small_bf16(threshold=0.7, batch=3)
+    h = _handle(cfg)
+    h.prefill(synth.prompt_np(cfg))
+    P, Bs, mask = cfg["prompt_len"], cfg["block_size"], cfg["mask_id"]
+    prev = h.get_tokens()
+    total = 0
+    for b in range(cfg["gen_length"] // Bs):
+        if b:
+            h.block_begin(b)
+        done = False
+        while not done:
+            n, done = h.denoise_step()
+            total += 1
+            x = h.get_tokens()
+            info = h.get_step_info()
+            was = prev != mask
+            assert np.array_equal(x[was], prev[was])
+            s = P + b * Bs
+            assert np.array_equal(x[:, s:s + Bs][info["committed"]], info["tok"][info["committed"]])
+            assert (n == info["committed"].sum(axis=1)).all()
+            assert (x[:, s + Bs:] == mask).all()
+            prev = x
+    assert total <= cfg["gen_length"]
+    assert (prev[:, P:] != mask).all()
+
+
+def test_deterministic_repeat():
+    cfg = small_bf16(batch=5, block_size=32, gen_length=64)
+    h = _handle(cfg)
+    xa, _ = h.generate(synth.prompt_np(cfg))
+    xb, _ = h.generate(synth.prompt_np(cfg))
+    assert np.array_equal(xa, xb)
+
+
+def test_call_order_errors():
+    from diffusion_block_denoise_amd import dllm
+    cfg = small_bf16()
+    h = _handle(cfg)
+    with pytest.raises(dllm.DllmError) as e:
+        h.block_begin(0)
+    assert e.value.code == dllm.DLLM_ESTATE
+    with pytest.raises(dllm.DllmError) as e:
+        h.denoise_step()
+    assert e.value.code == dllm.DLLM_ESTATE
+    bad = synth.prompt_np(cfg).copy()
+    bad[0, 0] = cfg["vocab"]
+    with pytest.raises(dllm.DllmError) as e:
+        h.prefill(bad)
+    assert e.value.code == dllm.DLLM_EINVAL
