@@ -6,7 +6,13 @@ the LLaDA-8B shape (32 layers, d_model 4096, 32 heads x 128, SwiGLU 12288, vocab
 seeded random-init bf16 weights, batch 1, a 512-token uniform random prompt, gen_length 256,
 block_size 32, threshold 0.9, dual prefix+suffix KV cache.
 
-Prints one JSON line.
+Prints one JSON line with:
+  value        committed tokens/s over the timed generates (inputs resident in HBM)
+  roofline     the kernel class with the most time in the timed region: algorithmic bytes
+               (HBM-bound class) or flops (MFMA-bound class) per launch over its average
+               HIP-event-measured duration, against MI355X's published peak
+  cpu_baseline the fp64 oracle timed on the host cores on a bounded sample of the same
+               workload, projected to tokens/s with this run's refresh/step counts
 """
 
 import argparse
@@ -18,9 +24,105 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def phase_latency(h, prompt, cfg):
+    """Median block-refresh and cached-step latency (ms), timed with events on the stream."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    h.prefill(prompt)
+    refresh, step = [], []
+    nb = cfg["gen_length"] // cfg["block_size"]
+    for b in range(nb):
+        if b:
+            e0, e1 = ev(), ev()
+            e0.record()
+            h.block_begin(b)
+            e1.record()
+            torch.cuda.synchronize()
+            refresh.append(e0.elapsed_time(e1))
+        first = True
+        done = False
+        while not done:
+            e0, e1 = ev(), ev()
+            e0.record()
+            _, done = h.denoise_step()
+            e1.record()
+            torch.cuda.synchronize()
+            if not first:
+                step.append(e0.elapsed_time(e1))
+            first = False
+    med = lambda v: sorted(v)[len(v) // 2] if v else None  # noqa: E731
+    return med(refresh), med(step)
+
+
+def roofline(prof, dtype):
+    """Roofline entry for the kernel class with the largest timed share."""
+    name, k = max(prof.items(), key=lambda kv: kv[1]["ms"])
+    if k["launches"] == 0 or k["ms"] <= 0:
+        return None, name
+    t = k["ms"] / 1e3
+    if name == "gemm_tiled":
+        peak = BF16_PEAK_TFLOPS if dtype == "bf16" else F32_PEAK_TFLOPS
+        ach = k["flops"] / t / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": None, "kernel": name,
+                "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
+    ach = k["bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": name,
+            "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
+
+
+def cpu_baseline(cfg, W, n_full, n_cached, sample_layers=2):
+    """The oracle on a bounded sample: `sample_layers` of the model's layers, one refresh forward
+    over all positions and one dual-cache step over the block rows of batch row 0, plus the
+    lm_head statistics; scaled by n_layers / sample_layers and projected with the GPU run's
+    refresh and cached-step counts."""
+    import numpy as np
+    import synth
+    from oracle import model as om
+    nl = cfg["n_layers"]
+    sc = dict(cfg, n_layers=sample_layers)
+    names = synth.configs.weight_names(sample_layers)
+    w_host = {n: W[n].float().cpu().numpy() for n in names}
+    m = om.Model(sc, w_host)
+    x = synth.block_state_np(cfg, 1)[0].astype(np.int64)
+    L = len(x)
+    s = cfg["prompt_len"] + cfg["block_size"]
+    e = s + cfg["block_size"]
+    cache = m.new_cache()
+    t0 = time.perf_counter()
+    hid = m.forward(x, 0, L, cache)
+    t_full = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    m.stats(hid[s:e])
+    t_stats = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hid = m.forward(x, s, e, cache)
+    t_step = time.perf_counter() - t0
+    scale = nl / sample_layers
+    T_refresh = t_full * scale + t_stats
+    T_step = t_step * scale + t_stats
+    total = cfg["batch"] * (n_full * T_refresh + n_cached * T_step)
+    tokens = cfg["batch"] * cfg["gen_length"]
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": tokens / total, "unit": "tokens/s (projected)", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": (f"{sample_layers} of {nl} layers, batch row 0: one refresh forward over "
+                       f"{L} positions ({t_full:.2f}s), one dual-cache step over "
+                       f"{cfg['block_size']} block rows ({t_step:.2f}s), lm_head statistics "
+                       f"({t_stats:.2f}s); per-layer times x{scale:g}, projected with "
+                       f"{n_full} refreshes + {n_cached} cached steps per batch row"),
+            "refresh_s": T_refresh, "step_s": T_step}
 
 
 def main():
@@ -33,10 +135,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(multi-GPU sharding is described, not built)", file=sys.stderr)
+              "(the multi-GPU sharding is a design note, not built)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
@@ -52,29 +153,51 @@ def main():
     prompt = synth.prompt_np(cfg)
     for i in range(args.warmup):
         _, st = h.generate(prompt)
-        log(f"warmup {i}: {st['steps']} steps")
+        log(f"warmup {i}: {st['steps']} denoise steps")
+    mask = (1 << dllm.DLLM_KC_GEMM_SKINNY) | (1 << dllm.DLLM_KC_GEMM_TILED) | \
+        (1 << dllm.DLLM_KC_ATTENTION)
+    h.set_profiling(mask)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    steps = []
+    stats = []
     for i in range(args.steps):
         _, st = h.generate(prompt)
-        steps.append(st)
+        stats.append(st)
         log(f"step {i}: {st['steps']} denoise steps")
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    prof = h.get_profile()
+    h.set_profiling(0)
     B, G = cfg["batch"], cfg["gen_length"]
     value = B * G * args.steps / el
+    roof, dom = roofline(prof, cfg["dtype"])
+    refresh_ms, step_ms = phase_latency(h, prompt, cfg)
+    st = stats[-1]
     out = {
         "metric": "committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded random-init weights, uniform random prompt)",
-        "config": {"workload": cfg["name"], "batch": B, "prompt_len": cfg["prompt_len"],
-                   "gen_length": G, "block_size": cfg["block_size"],
-                   "threshold": cfg["threshold"], "use_cache": "dual"},
-        "denoise_steps_per_generate": steps[-1]["steps"],
+        "config": {"workload": cfg["name"], "layers": cfg["n_layers"], "d_model": cfg["d_model"],
+                   "batch": B, "prompt_len": cfg["prompt_len"], "gen_length": G,
+                   "block_size": cfg["block_size"], "threshold": cfg["threshold"],
+                   "use_cache": ["none", "prefix", "dual"][cfg["use_cache"]]},
+        "roofline": roof,
+        "denoise_steps_per_generate": st["steps"],
+        "refreshes_per_generate": st["full_forwards"],
+        "cached_steps_per_generate": st["cached_forwards"],
+        "refresh_latency_ms": refresh_ms, "cached_step_latency_ms": step_ms,
+        "kernel_classes": {k: {"launches": v["launches"], "ms": v["ms"],
+                               "GB_per_s": v["bytes"] / (v["ms"] / 1e3) / 1e9 if v["ms"] else None,
+                               "TFLOP_per_s": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["ms"] else None}
+                           for k, v in prof.items()},
+        "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(cfg, W, st["full_forwards"], st["cached_forwards"])
+        log(f"cpu baseline sample took {time.time() - t0:.1f}s")
     print(json.dumps(out), flush=True)
 
 

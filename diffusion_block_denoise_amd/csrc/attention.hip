@@ -4,10 +4,13 @@
 // K/V head) pair.  Query rows of a pair are (position, head-in-group) combinations, so a group
 // of G query heads shares every K/V load.  The wave computes S^T = K Q^T over 32 keys at a time:
 // in the MFMA output each lane holds one query and 16 keys, so the row softmax needs a single
-// cross-half shuffle.  The probabilities P^T (rounded to bf16) are already laid out as the B
-// operand of the next MFMA, O^T += V^T P^T, whose A operand comes from the transposed V cache
+// cross-half shuffle.  The probabilities P^T are already laid out as the B operand of the next
+// MFMA, O^T += V^T P^T, whose A operand comes from the transposed V cache
 // ([hd][L] per head): every lane reads two runs of four consecutive keys.  No LDS is used.
-// The normaliser sums the rounded probabilities, so the weights applied to V sum to one.
+// q, K, V^T and P are bf16 hi/lo pairs (hi + lo carries about 16 mantissa bits): every product
+// is hi*hi + lo*hi + hi*lo in fp32 accumulators.  A single bf16 rounding of K, V, q or P moves
+// the 32-layer, d=4096 model's confidences by several percent; the pairs keep the attention at
+// fp32-like accuracy for 1.5x the MFMA work of one bf16 pass per operand pair.
 // When the tiles alone cannot fill the GPU (a cached step has few queries) the keys are split
 // into chunks; each chunk writes (O, running max, sum) and a merge kernel combines the chunks
 // in chunk order.
@@ -44,11 +47,10 @@ size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
 }
 
 template <int HD>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ q,
-                                                       const bf16 *__restrict__ kc,
-                                                       const bf16 *__restrict__ vt, RowSet rs,
-                                                       int H, int Hkv, int chunk, float scale_log2,
-                                                       bf16 *o_hi, bf16 *o_lo, float *part) {
+__global__ __launch_bounds__(64) void attn_mfma_kernel(
+    const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
+    const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
+    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part) {
   constexpr int KS = HD / 16;  // k-steps of the QK^T product
   constexpr int DB = HD / 32;  // 32-dim blocks of the output
   const int G = H / Hkv;
@@ -64,18 +66,22 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ 
   const int m = b * rs.nR + pi;
   const int ldq = H * HD;
 
-  bf16x8_t qf[KS];
+  // Q^T as the B operand: lane = query column, 8 dims per k-step.
+  bf16x8_t qh[KS], ql[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
+    const size_t o = (size_t)m * ldq + head * HD + kk * 16 + half * 8;
     if (valid) {
-      qf[kk] = *(const bf16x8_t *)(q + (size_t)m * ldq + head * HD + kk * 16 + half * 8);
+      qh[kk] = *(const bf16x8_t *)(q_hi + o);
+      ql[kk] = *(const bf16x8_t *)(q_lo + o);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+      for (int e = 0; e < 8; ++e) qh[kk][e] = ql[kk][e] = (__bf16)0.f;
     }
   }
-  const bf16 *K = kc + (size_t)bg * rs.Lp * HD;
-  const bf16 *V = vt + (size_t)bg * HD * rs.Lp;
+  const size_t kv_off = (size_t)bg * rs.Lp * HD;  // same for K [Lp][HD] and V^T [HD][Lp]
+  const bf16 *Kh = k_hi + kv_off, *Kl = k_lo + kv_off;
+  const bf16 *Vh = vt_hi + kv_off, *Vl = vt_lo + kv_off;
 
   float mrun = -INFINITY, lsum = 0.f;
   f32x16 o[DB];
@@ -87,14 +93,18 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ 
   const int kbeg = split * chunk;
   const int kend = min(rs.Lp, kbeg + chunk);
   for (int kb = kbeg; kb < kend; kb += 32) {
+    // S^T = K Q^T with hi/lo operands (the lo x lo term is below fp32 resolution).
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    const bf16 *krow = K + (size_t)(kb + col) * HD + half * 8;
+    const size_t krow = (size_t)(kb + col) * HD + half * 8;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8_t kf = *(const bf16x8_t *)(krow + kk * 16);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+      const bf16x8_t kh = *(const bf16x8_t *)(Kh + krow + kk * 16);
+      const bf16x8_t kl = *(const bf16x8_t *)(Kl + krow + kk * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kk], s, 0, 0, 0);
     }
     // s[i]: key kb + 8*(i/4) + 4*half + i%4, query col
     float tmax = -INFINITY;
@@ -107,13 +117,16 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ 
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
-    bf16x8_t pf[2];
+    // P^T as hi/lo B operands of the next product; register i of k-step i/8 holds key slot i%8.
+    bf16x8_t ph[2], pl[2];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const __bf16 pb = (__bf16)exp2f(s[i] - mnew);
-      pf[i >> 3][i & 7] = pb;
-      psum += (float)pb;
+      const float pv = exp2f(s[i] - mnew);
+      const __bf16 hi = (__bf16)pv;
+      ph[i >> 3][i & 7] = hi;
+      pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
+      psum += pv;
     }
     psum += __shfl_xor(psum, 32, 64);
     lsum = lsum * alpha + psum;
@@ -122,15 +135,22 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(const bf16 *__restrict__ 
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-      const bf16 *vrow = V + (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
+      const size_t vrow = (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x4_t v0 = *(const bf16x4_t *)(vrow + 16 * ks);
-        const bf16x4_t v1 = *(const bf16x4_t *)(vrow + 16 * ks + 8);
-        bf16x8_t vf;
+        const bf16x4_t h0 = *(const bf16x4_t *)(Vh + vrow + 16 * ks);
+        const bf16x4_t h1 = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8);
+        const bf16x4_t l0 = *(const bf16x4_t *)(Vl + vrow + 16 * ks);
+        const bf16x4_t l1 = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8);
+        bf16x8_t vh, vl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { vf[e] = v0[e]; vf[e + 4] = v1[e]; }
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[d], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          vh[e] = h0[e]; vh[e + 4] = h1[e];
+          vl[e] = l0[e]; vl[e + 4] = l1[e];
+        }
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl[ks], o[d], 0, 0, 0);
       }
     }
   }
@@ -239,8 +259,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   }
 }
 
-hipError_t launch_attention(const void *q, const void *k_cache, const void *vt_cache, RowSet rs,
-                            int H, int Hkv, int hd, bf16 *o_hi, bf16 *o_lo, float *o_f32,
+hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache,
+                            const void *k_cache_lo, const void *vt_cache, const void *vt_cache_lo,
+                            RowSet rs, int H, int Hkv, int hd, bf16 *o_hi, bf16 *o_lo, float *o_f32,
                             float *part, int dtype, hipStream_t st) {
   if (rs.M() <= 0) return hipSuccess;
   if (dtype == 0) {
@@ -258,7 +279,8 @@ hipError_t launch_attention(const void *q, const void *k_cache, const void *vt_c
 #define ATTN_CASE(HDV)                                                                          \
   case HDV:                                                                                     \
     hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \
-                       (const bf16 *)k_cache, (const bf16 *)vt_cache, rs, H, Hkv, chunk,        \
+                       (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,     \
+                       (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, chunk,    \
                        scale_log2, o_hi, o_lo, part);                                           \
     if (splits > 1)                                                                             \
       hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3(rs.B * Hkv * nqt * 32), dim3(64), 0, st,  \

@@ -59,9 +59,10 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return bad("rms_eps must be finite and >= 0");
   if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return bad("rope_base must be finite and > 0");
   if (!std::isfinite(c->logit_scale)) return bad("logit_scale must be finite");
+  if (c->d_model % 64 || c->d_model > 8192) return bad("d_model must be a multiple of 64 and <= 8192");
   if (c->dtype == DLLM_BF16) {
-    if (c->d_model % 64 || (c->n_heads * c->head_dim) % 64 || c->ffn_dim % 64)
-      return bad("bf16: d_model, n_heads*head_dim and ffn_dim must be multiples of 64");
+    if ((c->n_heads * c->head_dim) % 64 || c->ffn_dim % 64)
+      return bad("bf16: n_heads*head_dim and ffn_dim must be multiples of 64");
   }
   if (c->batch < 1) return bad("batch must be >= 1");
   if (c->prompt_len < 0) return bad("prompt_len must be >= 0");
@@ -85,12 +86,12 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
 // Workspace plan
 struct Plan {
   int B, P, G, Bs, L, Lp, NB, spb, d, H, Hkv, hd, F, V, nq, nkv, dt;
-  size_t esz;  // storage bytes per element (4 or 2)
+  size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
-      off_q, off_apart, off_gpart, off_cnt, off_hpart, off_tok, off_conf, off_p2, off_com,
+      off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
       off_ncom, off_rem, total;
   size_t kv_layer_elems;  // K (or V) elements per layer
-  int n_vtiles, max_tiles;
+  int n_vtiles;
 };
 
 RowSet rows_of(const Plan &p, int start, int nR) {
@@ -107,9 +108,8 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.d = c->d_model; p.H = c->n_heads; p.Hkv = c->n_kv_heads; p.hd = c->head_dim;
   p.F = c->ffn_dim; p.V = c->vocab; p.nq = p.H * p.hd; p.nkv = p.Hkv * p.hd;
   p.dt = c->dtype == DLLM_BF16 ? 1 : 0;
-  p.esz = p.dt ? 2 : 4;
   const size_t Mmax = (size_t)p.B * p.L;
-  const int wa = std::max(p.d, p.nq);
+  p.Mmax = Mmax;
   p.kv_layer_elems = (size_t)p.B * p.Hkv * p.Lp * p.hd;
 
   // Row counts that a forward can have: refresh / no cache (B*L), dual step (B*Bs), prefix
@@ -117,18 +117,13 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   std::vector<int> Ms = {p.B * p.L, p.B * p.Bs};
   for (int b = 0; b < p.NB; ++b) Ms.push_back(p.B * (p.L - (p.P + b * p.Bs)));
   size_t gpart = 0, apart = 0;
-  int max_tiles = 1;
   for (int M : Ms) {
     const int bn = gemm_bn(M, p.dt);
     const int ffn_virtual = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
     const int shapes[4][2] = {{p.nq + 2 * p.nkv, p.d}, {p.d, p.nq}, {ffn_virtual, p.d}, {p.d, p.F}};
     for (auto &s : shapes) {
       const int splits = gemm_num_splits(M, s[0], s[1], p.dt);
-      if (splits > 1) {
-        gpart = std::max(gpart, (size_t)splits * M * s[0] * sizeof(float));
-        const int bm = gemm_bm(M, p.dt);
-        max_tiles = std::max(max_tiles, ((M + bm - 1) / bm) * ((s[0] + bn - 1) / bn));
-      }
+      if (splits > 1) gpart = std::max(gpart, (size_t)splits * M * s[0] * sizeof(float));
     }
     const int nR = M / p.B;
     apart = std::max(apart, attention_part_bytes(rows_of(p, 0, nR), p.H, p.Hkv, p.hd, p.dt));
@@ -138,31 +133,28 @@ void make_plan(const dllm_cfg *c, Plan &p) {
     const int M = p.B * p.Bs, bn = gemm_bn(M, p.dt);
     p.n_vtiles = (p.V + bn - 1) / bn;
     const int splits = gemm_num_splits(M, p.V, p.d, p.dt);
-    if (splits > 1) {
-      gpart = std::max(gpart, (size_t)splits * M * p.V * sizeof(float));
-      const int bm = gemm_bm(M, p.dt);
-      max_tiles = std::max(max_tiles, ((M + bm - 1) / bm) * p.n_vtiles);
-    }
+    if (splits > 1) gpart = std::max(gpart, (size_t)splits * M * p.V * sizeof(float));
   }
-  p.max_tiles = max_tiles;
 
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
   p.off_x = take(Mmax * 4);
-  p.off_k = take(p.kv_layer_elems * c->n_layers * p.esz);
-  p.off_v = take(p.kv_layer_elems * c->n_layers * p.esz);
+  // K and V^T caches, per layer: fp32, or a bf16 hi plane followed by a bf16 lo plane
+  p.off_k = take(p.kv_layer_elems * c->n_layers * 4);
+  p.off_v = take(p.kv_layer_elems * c->n_layers * 4);
   p.off_cos = take((size_t)p.L * (p.hd / 2) * 4);
   p.off_sin = take((size_t)p.L * (p.hd / 2) * 4);
   p.off_h = take(Mmax * p.d * 4);
-  // GEMM inputs: bf16 hi/lo pairs, or one fp32 array in the hi slot
+  // GEMM input a: RMSNorm(h) [Mmax][d] or the attention output [Mmax][nq]; bf16 hi/lo planes,
+  // or fp32 in the hi slot
+  const size_t wa = std::max(p.d, p.nq);
   p.off_ahi = take(Mmax * wa * (p.dt ? 2 : 4));
   p.off_alo = take(p.dt ? Mmax * wa * 2 : 0);
   p.off_acthi = take(Mmax * p.F * (p.dt ? 2 : 4));
   p.off_actlo = take(p.dt ? Mmax * p.F * 2 : 0);
-  p.off_q = take(Mmax * p.nq * p.esz);
+  p.off_q = take(Mmax * p.nq * 4);  // fp32, or bf16 hi plane + lo plane
   p.off_apart = take(apart);
   p.off_gpart = take(gpart);
-  p.off_cnt = take((size_t)max_tiles * 4);
   p.off_hpart = take((size_t)p.B * p.Bs * p.n_vtiles * sizeof(HeadPart));
   p.off_tok = take((size_t)p.B * p.Bs * 4);
   p.off_conf = take((size_t)p.B * p.Bs * 4);
@@ -189,7 +181,6 @@ struct dllm_handle {
   float *cos_t, *sin_t, *h;
   void *a_hi, *a_lo, *act_hi, *act_lo, *q;
   float *apart, *gpart;
-  int *cnt;
   HeadPart *hpart;
   int *tok;
   float *conf, *p2;
@@ -204,6 +195,20 @@ struct dllm_handle {
   dllm_stats stats{};
   std::vector<int> h_rem, h_ncom;
   std::string err;
+  // per-kernel-class timing (dllm_set_profiling)
+  struct Pending {
+    int cls;
+    hipEvent_t b, e;
+    double bytes, flops;
+  };
+  int prof_mask = 0;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_next = 0;
+  std::vector<Pending> pending;
+  dllm_kernel_prof prof[DLLM_KC_COUNT] = {};
+  ~dllm_handle() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -219,7 +224,75 @@ namespace {
 
 inline const void *LW(dllm_t *h, int l, int j) { return h->layer[(size_t)9 * l + j]; }
 
-void *kv_layer(dllm_t *h, char *base, int l) { return base + (size_t)l * h->p.kv_layer_elems * h->p.esz; }
+// ---- per-kernel-class timing -------------------------------------------------------------------
+// Collect the durations of the pending event pairs (the stream has been synchronised).
+int prof_resolve(dllm_t *h) {
+  for (const auto &pd : h->pending) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, pd.b, pd.e));
+    dllm_kernel_prof &k = h->prof[pd.cls];
+    k.launches++;
+    k.ms += ms;
+    k.bytes += pd.bytes;
+    k.flops += pd.flops;
+  }
+  h->pending.clear();
+  h->ev_next = 0;
+  return DLLM_OK;
+}
+
+// Event pair for one launch of class cls, or nulls when that class is not being timed.
+int prof_events(dllm_t *h, int cls, hipEvent_t *b, hipEvent_t *e) {
+  *b = *e = nullptr;
+  if (cls < 0 || !(h->prof_mask & (1 << cls))) return DLLM_OK;
+  if (h->ev_next + 2 > h->ev_pool.size()) {
+    HIPCHK(hipStreamSynchronize(h->st));
+    int rc = prof_resolve(h);
+    if (rc) return rc;
+  }
+  *b = h->ev_pool[h->ev_next++];
+  *e = h->ev_pool[h->ev_next++];
+  return DLLM_OK;
+}
+
+void prof_push(dllm_t *h, int cls, hipEvent_t b, hipEvent_t e, double bytes, double flops) {
+  if (b) h->pending.push_back({cls, b, e, bytes, flops});
+}
+
+// Algorithmic work of a GEMM launch: each weight, A element and output element once.
+void gemm_work(dllm_t *h, const GemmArgs &g, int n_real, double out_bytes, double &bytes,
+               double &flops) {
+  const double esz = h->p.dt ? 2.0 : 4.0;  // weight element
+  bytes = (double)n_real * g.K * esz + (double)g.M * g.K * 4.0 + out_bytes;
+  flops = 2.0 * g.M * n_real * g.K;
+}
+
+int gemm_class(dllm_t *h, const GemmArgs &g) {
+  const int kind = gemm_kind(g.M, g.K, h->p.dt);
+  return kind == 1 ? DLLM_KC_GEMM_SKINNY : (kind == 2 ? DLLM_KC_GEMM_TILED : -1);
+}
+
+// launch_gemm with the timing bracket of its class.
+int run_gemm(dllm_t *h, const GemmArgs &g, int n_real, double out_bytes, int *splits) {
+  const int cls = gemm_class(h, g);
+  hipEvent_t b, e;
+  int rc = prof_events(h, cls, &b, &e);
+  if (rc) return rc;
+  HIPCHK(launch_gemm(g, h->p.dt, h->st, splits, b, e));
+  if (b) {
+    double bytes, flops;
+    gemm_work(h, g, n_real, out_bytes, bytes, flops);
+    prof_push(h, cls, b, e, bytes, flops);
+  }
+  return DLLM_OK;
+}
+
+// Layer l of a cache: fp32 array, or (bf16) the hi plane; lo plane follows the hi plane.
+void *kv_layer(dllm_t *h, char *base, int l) { return base + (size_t)l * h->p.kv_layer_elems * 4; }
+void *kv_layer_lo(dllm_t *h, char *base, int l) {
+  return (char *)kv_layer(h, base, l) + h->p.kv_layer_elems * 2;
+}
+void *q_lo(dllm_t *h) { return (char *)h->q + h->p.Mmax * h->p.nq * 2; }
 
 GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M, int N, int K) {
   GemmArgs g;
@@ -233,12 +306,32 @@ GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M
   g.lda = lda;
   g.M = M; g.N = N; g.K = K;
   g.partial = h->gpart;
-  g.counters = h->cnt;
   g.scale = 1.f;
   return g;
 }
 
-// One forward over row set rs: embedding, n_layers blocks, hidden states left in h.
+void set_resid(dllm_t *h, GemmArgs &g) {
+  g.epi = EPI_RESID;
+  g.resid = h->h;
+  g.ld_out = h->p.d;
+}
+
+// Residual GEMM followed by the split-K fold and the next RMSNorm (gain) into a.
+int resid_gemm_norm(dllm_t *h, GemmArgs &g, const void *gain) {
+  const Plan &p = h->p;
+  const bool bf = p.dt == 1;
+  int splits = 1;
+  int rc = run_gemm(h, g, g.N, 8.0 * g.M * g.N, &splits);  // h read and written
+  if (rc) return rc;
+  HIPCHK(launch_resid_norm(g.M, p.d, h->h, splits > 1 ? h->gpart : nullptr, splits > 1 ? splits : 0,
+                           gain, h->cfg.rms_eps, bf ? (bf16 *)h->a_hi : nullptr,
+                           bf ? (bf16 *)h->a_lo : nullptr, bf ? nullptr : (float *)h->a_hi, p.dt,
+                           h->st));
+  return DLLM_OK;
+}
+
+// One forward over row set rs.  Afterwards h holds the final residual stream and a holds
+// RMSNorm(h) with the final-norm gain (the lm_head input).
 int forward(dllm_t *h, RowSet rs) {
   const Plan &p = h->p;
   const dllm_cfg &c = h->cfg;
@@ -249,10 +342,7 @@ int forward(dllm_t *h, RowSet rs) {
   HIPCHK(launch_embed_norm(h->x, h->embed, LW(h, 0, 0), rs, p.d, c.rms_eps, h->h, bf ? ahi : nullptr,
                            bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
   for (int l = 0; l < c.n_layers; ++l) {
-    if (l > 0)
-      HIPCHK(launch_rmsnorm(h->h, LW(h, l, 0), M, M, 0, 0, p.d, c.rms_eps, bf ? ahi : nullptr,
-                            bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
-    // Q, K, V projections; rotary embedding; K/V to the cache slots of rows rs
+    // Q, K, V projections of a; rotary embedding; K/V to the cache slots of rows rs
     {
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.nq + 2 * p.nkv, p.d);
       g.w[0] = LW(h, l, 1); g.w[1] = LW(h, l, 2); g.w[2] = LW(h, l, 3);
@@ -263,20 +353,42 @@ int forward(dllm_t *h, RowSet rs) {
       g.q_out = h->q;
       g.k_cache = kv_layer(h, h->kc, l);
       g.vt_cache = kv_layer(h, h->vc, l);
-      HIPCHK(launch_gemm(g, p.dt, h->st));
+      if (bf) {
+        g.q_out_lo = q_lo(h);
+        g.k_cache_lo = kv_layer_lo(h, h->kc, l);
+        g.vt_cache_lo = kv_layer_lo(h, h->vc, l);
+      }
+      int rc = run_gemm(h, g, g.N, 4.0 * M * g.N, nullptr);  // q, K, V as 4-byte pairs
+      if (rc) return rc;
     }
     // attention over all cached positions -> a (input of the output projection)
-    HIPCHK(launch_attention(h->q, kv_layer(h, h->kc, l), kv_layer(h, h->vc, l), rs, p.H, p.Hkv, p.hd,
-                            bf ? ahi : nullptr, bf ? alo : nullptr, bf ? nullptr : af, h->apart, p.dt,
-                            h->st));
+    {
+      hipEvent_t eb, ee;
+      int rc = prof_events(h, DLLM_KC_ATTENTION, &eb, &ee);
+      if (rc) return rc;
+      if (eb) HIPCHK(hipEventRecord(eb, h->st));
+      HIPCHK(launch_attention(h->q, bf ? q_lo(h) : nullptr, kv_layer(h, h->kc, l),
+                              bf ? kv_layer_lo(h, h->kc, l) : nullptr, kv_layer(h, h->vc, l),
+                              bf ? kv_layer_lo(h, h->vc, l) : nullptr, rs, p.H, p.Hkv, p.hd,
+                              bf ? ahi : nullptr, bf ? alo : nullptr, bf ? nullptr : af, h->apart,
+                              p.dt, h->st));
+      if (ee) {
+        HIPCHK(hipEventRecord(ee, h->st));
+        // K and V of every cached position once per (batch row, K/V head), q in, o out
+        const double kv = 2.0 * p.B * p.Hkv * (double)p.L * p.hd * 4.0;
+        const double qo = 2.0 * M * p.nq * 4.0;
+        prof_push(h, DLLM_KC_ATTENTION, eb, ee, kv + qo, 4.0 * M * p.H * (double)p.L * p.hd);
+      }
+    }
+    // output projection + residual; a = ffn RMSNorm(h)
     {
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.nq, M, p.d, p.nq);
       g.w[0] = LW(h, l, 4); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
-      g.epi = EPI_RESID; g.resid = h->h; g.ld_out = p.d;
-      HIPCHK(launch_gemm(g, p.dt, h->st));
+      set_resid(h, g);
+      int rc = resid_gemm_norm(h, g, LW(h, l, 5));
+      if (rc) return rc;
     }
-    HIPCHK(launch_rmsnorm(h->h, LW(h, l, 5), M, M, 0, 0, p.d, c.rms_eps, bf ? ahi : nullptr,
-                          bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+    // gate/up + SwiGLU -> act
     {
       const int bn = gemm_bn(M, p.dt);
       const int nvirt = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
@@ -287,13 +399,16 @@ int forward(dllm_t *h, RowSet rs) {
       g.ld_act = p.F;
       if (bf) { g.act_hi = (bf16 *)h->act_hi; g.act_lo = (bf16 *)h->act_lo; }
       else g.act_f32 = (float *)h->act_hi;
-      HIPCHK(launch_gemm(g, p.dt, h->st));
+      int rc = run_gemm(h, g, 2 * p.F, 4.0 * M * p.F, nullptr);  // act as a 4-byte pair
+      if (rc) return rc;
     }
+    // down projection + residual; a = next layer's attention RMSNorm(h), or the final norm
     {
       GemmArgs g = gemm_base(h, h->act_hi, h->act_lo, p.F, M, p.d, p.F);
       g.w[0] = LW(h, l, 8); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
-      g.epi = EPI_RESID; g.resid = h->h; g.ld_out = p.d;
-      HIPCHK(launch_gemm(g, p.dt, h->st));
+      set_resid(h, g);
+      int rc = resid_gemm_norm(h, g, l + 1 < c.n_layers ? LW(h, l + 1, 0) : h->final_norm);
+      if (rc) return rc;
     }
   }
   h->last_rows = rs;
@@ -301,30 +416,27 @@ int forward(dllm_t *h, RowSet rs) {
   return DLLM_OK;
 }
 
-// Final norm of the block rows of the last forward into a (rows 0..B*Bs-1).
-int final_norm_block(dllm_t *h) {
+// A operand = the block rows of a after the last forward (final RMSNorm), rows 0..B*Bs-1.
+void set_block_rows(dllm_t *h, GemmArgs &g) {
   const Plan &p = h->p;
   const RowSet rs = h->last_rows;
-  const int s = p.P + h->block * p.Bs;
-  const bool bf = p.dt == 1;
-  HIPCHK(launch_rmsnorm(h->h, h->final_norm, p.B * p.Bs, p.Bs, rs.nR, s - rs.start, p.d,
-                        h->cfg.rms_eps, bf ? (bf16 *)h->a_hi : nullptr, bf ? (bf16 *)h->a_lo : nullptr,
-                        bf ? nullptr : (float *)h->a_hi, p.dt, h->st));
-  return DLLM_OK;
+  g.row_per = p.Bs;
+  g.row_stride = rs.nR;
+  g.row_off = p.P + h->block * p.Bs - rs.start;
 }
 
 // Statistics of the block rows: fused lm_head + per-tile softmax partials, then the merge.
 int head(dllm_t *h) {
   const Plan &p = h->p;
-  int rc = final_norm_block(h);
-  if (rc) return rc;
   const int M = p.B * p.Bs;
   GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
+  set_block_rows(h, g);
   g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
   g.epi = EPI_LMHEAD;
   g.scale = h->cfg.logit_scale;
   g.head_part = h->hpart; g.n_vtiles = p.n_vtiles; g.vocab = p.V; g.mask_id = h->cfg.mask_id;
-  HIPCHK(launch_gemm(g, p.dt, h->st));
+  int rc = run_gemm(h, g, p.V, (double)M * p.n_vtiles * sizeof(HeadPart), nullptr);
+  if (rc) return rc;
   HIPCHK(launch_head_merge(h->hpart, M, p.n_vtiles, h->tok, h->conf, h->p2, h->st));
   return DLLM_OK;
 }
@@ -394,6 +506,10 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   HIPCHK(hipMemcpyAsync(h->h_ncom.data(), h->ncom, p.B * 4, hipMemcpyDeviceToHost, h->st));
   HIPCHK(hipMemcpyAsync(h->h_rem.data(), h->rem, p.B * 4, hipMemcpyDeviceToHost, h->st));
   HIPCHK(hipStreamSynchronize(h->st));
+  if (!h->pending.empty()) {
+    int prc = prof_resolve(h);
+    if (prc) return prc;
+  }
   h->j++;
   h->stats.steps++;
   int done = 1;
@@ -468,7 +584,6 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->q = ws + p.off_q;
   h->apart = (float *)(ws + p.off_apart);
   h->gpart = (float *)(ws + p.off_gpart);
-  h->cnt = (int *)(ws + p.off_cnt);
   h->hpart = (HeadPart *)(ws + p.off_hpart);
   h->tok = (int *)(ws + p.off_tok);
   h->conf = (float *)(ws + p.off_conf); h->p2 = (float *)(ws + p.off_p2);
@@ -476,7 +591,7 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->ncom = (int *)(ws + p.off_ncom); h->rem = (int *)(ws + p.off_rem);
   h->h_rem.assign(p.B, 0);
   h->h_ncom.assign(p.B, 0);
-  // Zero the K/V cache (its padding slots must hold zeros) and the split-K counters; rotary table.
+  // Zero the K/V cache (its padding slots must hold zeros); rotary table.
   auto fail = [&](hipError_t e, const char *what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
     delete h;
@@ -485,8 +600,6 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   hipError_t e;
   if ((e = launch_fill_u32((uint32_t *)h->kc, 0, (p.off_cos - p.off_k) / 4, h->st)) != hipSuccess)
     return fail(e, "zero cache");
-  if ((e = launch_fill_u32((uint32_t *)h->cnt, 0, (size_t)p.max_tiles, h->st)) != hipSuccess)
-    return fail(e, "zero counters");
   if ((e = launch_rope_table(h->cos_t, h->sin_t, p.L, p.hd, cfg->rope_base, h->st)) != hipSuccess)
     return fail(e, "rope table");
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return fail(e, "synchronize");
@@ -581,13 +694,12 @@ int dllm_debug_block_logits(dllm_t *h, float *logits_dev) {
   if (!h || !logits_dev) return DLLM_EINVAL;
   if (!h->any_forward) { h->err = "no forward yet"; return DLLM_ESTATE; }
   const Plan &p = h->p;
-  int rc = final_norm_block(h);
-  if (rc) return rc;
   const int M = p.B * p.Bs;
   GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
+  set_block_rows(h, g);
   g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
   g.epi = EPI_STORE; g.out_f32 = logits_dev; g.ld_out = p.V; g.scale = h->cfg.logit_scale;
-  HIPCHK(launch_gemm(g, p.dt, h->st));
+  HIPCHK(launch_gemm(g, p.dt, h->st, nullptr));
   HIPCHK(launch_mask_column(logits_dev, M, p.V, h->cfg.mask_id, h->st));
   HIPCHK(hipStreamSynchronize(h->st));
   return DLLM_OK;
@@ -596,6 +708,30 @@ int dllm_debug_block_logits(dllm_t *h, float *logits_dev) {
 int dllm_get_stats(dllm_t *h, dllm_stats *stats) {
   if (!h || !stats) return DLLM_EINVAL;
   *stats = h->stats;
+  return DLLM_OK;
+}
+
+int dllm_set_profiling(dllm_t *h, int class_mask) {
+  if (!h) return DLLM_EINVAL;
+  if (class_mask & ~((1 << DLLM_KC_COUNT) - 1)) { h->err = "unknown kernel class"; return DLLM_EINVAL; }
+  HIPCHK(hipStreamSynchronize(h->st));
+  h->pending.clear();
+  h->ev_next = 0;
+  for (auto &k : h->prof) k = dllm_kernel_prof{};
+  if (class_mask && h->ev_pool.empty()) {
+    h->ev_pool.resize(4096);
+    for (auto &e : h->ev_pool) HIPCHK(hipEventCreate(&e));
+  }
+  h->prof_mask = class_mask;
+  return DLLM_OK;
+}
+
+int dllm_get_profile(dllm_t *h, dllm_kernel_prof *out) {
+  if (!h || !out) return DLLM_EINVAL;
+  HIPCHK(hipStreamSynchronize(h->st));
+  int rc = prof_resolve(h);
+  if (rc) return rc;
+  for (int i = 0; i < DLLM_KC_COUNT; ++i) out[i] = h->prof[i];
   return DLLM_OK;
 }
 

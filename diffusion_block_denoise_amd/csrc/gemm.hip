@@ -1,18 +1,21 @@
 // GEMM C[m][n] = sum_k A[m][k] * W[n][k] for the projections, the feed-forward and the lm_head,
-// with fused epilogues.  W is in torch Linear layout [out, in], so both operands are K-contiguous.
+// with fused epilogues.  W is in torch Linear layout [out, in], so both operands are
+// K-contiguous.
 //
-// bf16 path: A arrives as two bf16 arrays (hi, lo) with hi + lo equal to the fp32 activation to
-// about 16 mantissa bits; each K step issues two bf16 MFMAs (hi x W, lo x W) into one fp32
-// accumulator.  At the small row counts of a cached step the GEMM is bound by streaming W from
-// HBM, so the second MFMA costs no time and keeps the activation error at fp32 level.
+// A operand, bf16 path: two bf16 values (hi, lo) per element with hi + lo equal to the fp32
+// activation to about 16 mantissa bits; each K step issues two bf16 MFMAs (hi x W, lo x W) into
+// one fp32 accumulator.  At the row counts of a cached step the GEMM is bound by streaming W
+// from HBM, so the second MFMA costs no time and keeps the activation error at fp32 level.
 //
 // Tiles are staged through LDS.  After the K loop the wave accumulators are written to an fp32
 // C tile in LDS so that every epilogue has random access to the whole tile (rotary pairs i and
 // i + hd/2, gate and up halves, row-wise softmax over a vocabulary tile).  Split-K: every split
-// writes its tile to a partial buffer; the last split to arrive (per-tile atomic counter) sums
-// the partials in split order (deterministic), resets the counter and runs the epilogue.
+// writes its tile to a partial buffer and a reduce kernel sums the splits in split order
+// (deterministic) and runs the epilogue; for the residual add that reduce is the caller's
+// resid_norm kernel, which also applies the next RMSNorm.
 #include "kernels.h"
 
+#include <algorithm>
 #include <float.h>
 #include <limits.h>
 
@@ -20,6 +23,8 @@ namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 static constexpr int NT = 256;  // threads per workgroup (4 waves)
 
@@ -42,6 +47,12 @@ __device__ inline const T *w_row(const GemmArgs &a, int bn, int n0, int c) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// A operand loading: row m of A is row a_row(m) of the hi/lo planes.
+__device__ inline int a_row(const GemmArgs &a, int m) {
+  return a.row_per ? (m / a.row_per) * a.row_stride + a.row_off + m % a.row_per : m;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Epilogues over an fp32 C tile in LDS (ld = ldc).  T is the storage type of q and the cache.
 __device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -50,9 +61,17 @@ __device__ inline void split_hilo(float v, bf16 &hi, bf16 &lo) {
   lo = __float2bfloat16(v - __bfloat162float(hi));
 }
 
-template <typename T> __device__ inline T to_store(float v);
-template <> __device__ inline float to_store<float>(float v) { return v; }
-template <> __device__ inline bf16 to_store<bf16>(float v) { return __float2bfloat16(v); }
+// Store v at element i of an fp32 array, or of a bf16 hi/lo plane pair.
+template <typename T> __device__ inline void store_val(void *p, void *p_lo, size_t i, float v);
+template <> __device__ inline void store_val<float>(void *p, void *, size_t i, float v) {
+  ((float *)p)[i] = v;
+}
+template <> __device__ inline void store_val<bf16>(void *p, void *p_lo, size_t i, float v) {
+  bf16 hi, lo;
+  split_hilo(v, hi, lo);
+  ((bf16 *)p)[i] = hi;
+  ((bf16 *)p_lo)[i] = lo;
+}
 
 struct HeadAcc {
   float m1; int idx; float m2;
@@ -98,14 +117,14 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
           const float y = i < half ? x * cs - Ct[r * ldc + c + half] * sn
                                    : x * cs + Ct[r * ldc + c - half] * sn;
           if (n < nq) {
-            ((T *)a.q_out)[(size_t)m * nq + n] = to_store<T>(y);
+            store_val<T>(a.q_out, a.q_out_lo, (size_t)m * nq + n, y);
           } else {
             const int kvh = (n - nq) / hd;
-            ((T *)a.k_cache)[(((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i] = to_store<T>(y);
+            store_val<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
           }
         } else {
           const int kvh = (n - nq - nk) / hd;
-          ((T *)a.vt_cache)[(((size_t)b * Hkv + kvh) * hd + i) * rs.Lp + p] = to_store<T>(x);
+          store_val<T>(a.vt_cache, a.vt_cache_lo, (((size_t)b * Hkv + kvh) * hd + i) * rs.Lp + p, x);
         }
       }
     } break;
@@ -165,44 +184,46 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
   }
 }
 
-// Split-K: publish this split's tile, and let the last arriving split reduce all of them in
-// split order into Ct.  Returns false for the splits that are not last.
+// Split-K: each split writes its tile to partial[split][M][N]; a reduce kernel sums the splits
+// in split order (deterministic) and runs the epilogue.  No cross-workgroup fence: on a
+// multi-XCD GPU an agent-scope release fence writes back the XCD's L2, which costs far more
+// than the separate launch.
 template <int BM, int BN>
-__device__ bool splitk_fixup(const GemmArgs &a, float *Ct, int ldc, int m0, int n0) {
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int splits = gridDim.z;
-  const size_t MN = (size_t)a.M * a.N;
-  float *P = a.partial + (size_t)blockIdx.z * MN;
-  for (int e = tid; e < BM * BN; e += NT) {
+__device__ void write_partial(const GemmArgs &a, const float *Ct, int ldc, int m0, int n0) {
+  float *P = a.partial + (size_t)blockIdx.z * a.M * a.N;
+  for (int e = threadIdx.x; e < BM * BN; e += NT) {
     const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
     if (m < a.M && n < a.N) P[(size_t)m * a.N + n] = Ct[r * ldc + c];
   }
-  __threadfence();
-  __syncthreads();
-  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  if (tid == 0) s_last = (atomicAdd(&a.counters[tile], 1) == splits - 1);
-  __syncthreads();
-  if (!s_last) return false;
-  __threadfence();
-  for (int e = tid; e < BM * BN; e += NT) {
-    const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
-    float s = 0.f;
-    if (m < a.M && n < a.N) {
-      for (int z = 0; z < splits; ++z)
-        s += __hip_atomic_load(a.partial + z * MN + (size_t)m * a.N + n, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static constexpr int RD_BM = 8, RD_BN = 128;
+
+// Tile reduce for the epilogues that need a whole tile (rotary pairs, gate/up halves, lm_head
+// softmax partials): 8 x 128 tiles, 4 consecutive columns per thread.
+__global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int splits) {
+  constexpr int LDC = RD_BN + 4;
+  __shared__ float Ct[RD_BM * LDC];
+  const int m0 = blockIdx.y * RD_BM, n0 = blockIdx.x * RD_BN;
+  const size_t MN = (size_t)a.M * a.N;
+  const int r = threadIdx.x / (RD_BN / 4), c = (threadIdx.x % (RD_BN / 4)) * 4;
+  const int m = m0 + r, n = n0 + c;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (m < a.M && n < a.N) {  // N is a multiple of 4 (widths are multiples of 64)
+    const float *p = a.partial + (size_t)m * a.N + n;
+    for (int z = 0; z < splits; ++z) {
+      const float4 v = *(const float4 *)(p + z * MN);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
-    Ct[r * ldc + c] = s;
   }
-  if (tid == 0) a.counters[tile] = 0;
+  *(float4 *)(Ct + r * LDC + c) = s;
   __syncthreads();
-  return true;
+  run_epilogue<bf16, RD_BM, RD_BN>(a, Ct, LDC, m0, n0);
 }
 
 // ---------------------------------------------------------------------------------------------
-// bf16 MFMA kernel.  4 waves as WM x WN; each wave owns (BM/WM) x (BN/WN) of the tile in
-// 32x32 blocks (v_mfma_f32_32x32x16_bf16).  BK = 64.
+// Tiled bf16 MFMA kernel for many rows (block refresh).  4 waves as WM x WN; each wave owns
+// (BM/WM) x (BN/WN) of the tile in 32x32 blocks (v_mfma_f32_32x32x16_bf16).  BK = 64.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
   constexpr int BK = 64, LDK = BK + 8;  // row pitch in bf16 elements (pad 16 B)
@@ -223,48 +244,50 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
   const int kbeg = blockIdx.z * a.k_split;
   const int kend = min(a.K, kbeg + a.k_split);
 
-  // Global -> register staging: 16-byte chunks, 8 per 64-wide row.
-  constexpr int A_CH = BM * BK / 8 / NT;  // chunks per thread for each of hi, lo
+  // Global -> register staging: 16-byte chunks, 8 per 64-wide row.  Native vector types: arrays
+  // of HIP's uint4 struct defeat register promotion and end up in scratch memory.
+  constexpr int A_CH = BM * BK / 8 / NT;
   constexpr int W_CH = BN * BK / 8 / NT;
   static_assert(A_CH >= 1 && W_CH >= 1, "tile too small");
-  uint4 ra_hi[A_CH], ra_lo[A_CH], rw[W_CH];
+  s16x8 ra_hi[A_CH], ra_lo[A_CH], rw[W_CH];
   const uint16_t *wrow[W_CH];
 #pragma unroll
   for (int i = 0; i < W_CH; ++i) {
     const int ch = tid + i * NT, r = ch / 8;
     wrow[i] = w_row<uint16_t>(a, BN, n0, r);
   }
+  // A row offsets, hoisted out of the K loop (rows past M read row M-1; they only feed output
+  // rows that are never written)
+  size_t aoff[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int ch = tid + i * NT, r = ch / 8, c8 = (ch % 8) * 8;
+    aoff[i] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda + c8;
+  }
 
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int ch = tid + i * NT, r = ch / 8, c8 = (ch % 8) * 8, m = m0 + r;
-      if (m < a.M) {
-        const size_t off = (size_t)m * a.lda + k0 + c8;
-        ra_hi[i] = *(const uint4 *)((const uint16_t *)a.a_hi + off);
-        ra_lo[i] = *(const uint4 *)((const uint16_t *)a.a_lo + off);
-      } else {
-        ra_hi[i] = make_uint4(0, 0, 0, 0);
-        ra_lo[i] = make_uint4(0, 0, 0, 0);
-      }
+      ra_hi[i] = *(const s16x8 *)((const uint16_t *)a.a_hi + aoff[i] + k0);
+      ra_lo[i] = *(const s16x8 *)((const uint16_t *)a.a_lo + aoff[i] + k0);
     }
 #pragma unroll
     for (int i = 0; i < W_CH; ++i) {
       const int ch = tid + i * NT, c8 = (ch % 8) * 8;
-      rw[i] = wrow[i] ? *(const uint4 *)(wrow[i] + k0 + c8) : make_uint4(0, 0, 0, 0);
+      rw[i] = wrow[i] ? *(const s16x8 *)(wrow[i] + k0 + c8) : (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
   auto store = [&]() {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int ch = tid + i * NT, r = ch / 8, c8 = (ch % 8) * 8;
-      *(uint4 *)(As_hi + r * LDK + c8) = ra_hi[i];
-      *(uint4 *)(As_lo + r * LDK + c8) = ra_lo[i];
+      *(s16x8 *)(As_hi + r * LDK + c8) = ra_hi[i];
+      *(s16x8 *)(As_lo + r * LDK + c8) = ra_lo[i];
     }
 #pragma unroll
     for (int i = 0; i < W_CH; ++i) {
       const int ch = tid + i * NT, r = ch / 8, c8 = (ch % 8) * 8;
-      *(uint4 *)(Ws + r * LDK + c8) = rw[i];
+      *(s16x8 *)(Ws + r * LDK + c8) = rw[i];
     }
   };
 
@@ -277,12 +300,14 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int frow = lane & 31, fk = (lane >> 5) * 8;
-  if (kbeg < kend) load(kbeg);
+  // Loads are unconditional (the last iteration re-reads its own tile, unused) so the staging
+  // registers stay in registers and the wait counts stay static.
+  load(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     __syncthreads();
     store();
     __syncthreads();
-    if (k0 + BK < kend) load(k0 + BK);
+    load(min(k0 + BK, kend - BK));
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t fa_hi[TM], fa_lo[TM], fb[TN];
@@ -320,8 +345,138 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
         Ct[row * LDC + col] = acc[i][j][r];
       }
   __syncthreads();
-  if (gridDim.z > 1 && !splitk_fixup<BM, BN>(a, Ct, LDC, m0, n0)) return;
+  if (gridDim.z > 1) {
+    write_partial<BM, BN>(a, Ct, LDC, m0, n0);
+    return;
+  }
   run_epilogue<bf16, BM, BN>(a, Ct, LDC, m0, n0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Weight-streaming bf16 kernel for few rows (M <= 16*MT <= 64): the shape of a cached step, where
+// the time is the HBM read of W.  4 waves x 32 W rows = 128 columns per workgroup.
+//   W: each lane loads straight into the B-operand registers of v_mfma_f32_16x16x32_bf16 (lane:
+//      row l%16 of a 16-row block, 8 consecutive k at 8*(l/16) of each 32-wide k step; 4 lanes
+//      read 64 contiguous bytes of a row), through a ring of SK_D chunks of 64 k.
+//   A: shared by the 4 waves through LDS, one stage of SK_KA k at a time; the next stage is
+//      loaded into registers while the current one is consumed.
+// Every load is issued unconditionally and no loaded value is selected on, so the wait counts
+// are static and the W ring is only waited on one stage at a time.  Out-of-range addresses are
+// clamped instead: a W row past N or an A row past M only feeds output columns or rows that the
+// epilogue never writes, and the K range of a workgroup is a whole number of stages (K and the
+// split length are multiples of SK_KA).
+static constexpr int SK_BN = 128, SK_KA = 256, SK_D = SK_KA / 64;
+
+template <int MT>
+__global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
+  constexpr int BM = 16 * MT;
+  constexpr int LDA = SK_KA + 8;
+  constexpr int LDC = SK_BN + 4;
+  constexpr int A_BYTES = 2 * BM * LDA * 2, C_BYTES = BM * LDC * 4;
+  constexpr int SMEM = A_BYTES > C_BYTES ? A_BYTES : C_BYTES;
+  constexpr int ACH = BM * SK_KA / 8 / NT;  // 16-byte A chunks per thread per stage (hi and lo each)
+  static_assert(ACH >= 1, "stage too small");
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  uint16_t *Ah = (uint16_t *)smem;
+  uint16_t *Al = Ah + BM * LDA;
+  float *Ct = (float *)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rn = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * SK_BN;
+  const int kbeg = blockIdx.z * a.k_split;
+  const int kend = min(a.K, kbeg + a.k_split);
+  const int nchunk = (kend - kbeg) / 64;
+  const int nstage = (nchunk + SK_D - 1) / SK_D;
+
+  // W rows of this lane (a row past N reads row 0 of segment 0)
+  const uint16_t *wr[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    wr[cb] = w_row<uint16_t>(a, SK_BN, n0, wave * 32 + cb * 16 + rn);
+    if (!wr[cb]) wr[cb] = (const uint16_t *)a.w[0];
+  }
+  s16x8 wb[SK_D][2][2];
+  auto load_w = [&](int slot, int c) {
+    const int k = kbeg + min(c, nchunk - 1) * 64 + 8 * g;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) wb[slot][cb][ks] = *(const s16x8 *)(wr[cb] + k + 32 * ks);
+  };
+  // A stage prefetch: chunk e of the stage -> row e / (SK_KA/8), column 8 * (e % (SK_KA/8))
+  s16x8 rah[ACH], ral[ACH];
+  size_t aoff[ACH];  // row offsets, hoisted out of the stage loop
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int e = tid + i * NT, r = e / (SK_KA / 8), c8 = (e % (SK_KA / 8)) * 8;
+    aoff[i] = (size_t)a_row(a, min(r, a.M - 1)) * a.lda + kbeg + c8;
+  }
+  auto load_a = [&](int st) {
+    const int k = min(st, nstage - 1) * SK_KA;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      rah[i] = *(const s16x8 *)((const uint16_t *)a.a_hi + aoff[i] + k);
+      ral[i] = *(const s16x8 *)((const uint16_t *)a.a_lo + aoff[i] + k);
+    }
+  };
+  auto store_a = [&]() {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int e = tid + i * NT, r = e / (SK_KA / 8), c8 = (e % (SK_KA / 8)) * 8;
+      *(s16x8 *)(Ah + r * LDA + c8) = rah[i];
+      *(s16x8 *)(Al + r * LDA + c8) = ral[i];
+    }
+  };
+
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  load_a(0);
+#pragma unroll
+  for (int sl = 0; sl < SK_D; ++sl) load_w(sl, sl);
+  for (int st = 0; st < nstage; ++st) {
+    store_a();
+    __syncthreads();
+    load_a(st + 1);  // past the last stage this re-reads a clamped address; the values go unused
+#pragma unroll
+    for (int sl = 0; sl < SK_D; ++sl) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const int row = i * 16 + rn, col = sl * 64 + 32 * ks + 8 * g;
+          const bf16x8_t fh = *(const bf16x8_t *)(Ah + row * LDA + col);
+          const bf16x8_t fl = *(const bf16x8_t *)(Al + row * LDA + col);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            const bf16x8_t w8 = (bf16x8_t)wb[sl][cb][ks];
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fh, w8, acc[i][cb], 0, 0, 0);
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl, w8, acc[i][cb], 0, 0, 0);
+          }
+        }
+      }
+      load_w(sl, (st + 1) * SK_D + sl);
+    }
+    __syncthreads();
+  }
+  // 16x16 block layout: lane l, reg r -> row 4*(l/16) + r, column l%16.
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Ct[(i * 16 + 4 * g + r) * LDC + wave * 32 + cb * 16 + rn] = acc[i][cb][r];
+  __syncthreads();
+  if (gridDim.z > 1) {
+    write_partial<BM, SK_BN>(a, Ct, LDC, 0, n0);
+    return;
+  }
+  run_epilogue<bf16, BM, SK_BN>(a, Ct, LDC, 0, n0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -343,7 +498,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmArgs a) {
   for (int k0 = 0; k0 < a.K; k0 += BK) {
     for (int i = 0; i < 4; ++i) {
       const int e = tid + i * NT, r = e / 16, kk = e % 16, m = m0 + r, k = k0 + kk;
-      As[kk][r] = (m < a.M && k < a.K) ? a.a_f32[(size_t)m * a.lda + k] : 0.f;
+      As[kk][r] = (m < a.M && k < a.K) ? a.a_f32[(size_t)a_row(a, m) * a.lda + k] : 0.f;
       Ws[kk][r] = (wr[i] && k < a.K) ? wr[i][k] : 0.f;
     }
     __syncthreads();
@@ -366,45 +521,83 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmArgs a) {
 // ---------------------------------------------------------------------------------------------
 int gemm_bn(int M, int dtype) { return dtype == 0 ? 64 : 128; }
 
-int gemm_bm(int M, int dtype) {
-  if (dtype == 0) return 64;
-  return M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+// The skinny kernel serves M <= 64 (16-row blocks) when K is a whole number of its 256-wide
+// stages; otherwise 128 x 128 tiles.
+static bool use_skinny(int M, int K) { return M <= 64 && K % SK_KA == 0; }
+
+static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16) : 128; }
+
+// Split-K plan.  Skinny kernel: as many splits as keep the grid within one round of resident
+// workgroups (3 per CU up to 32 rows, 2 up to 48, 1 at 64), at least 512 k per split and at
+// most 8 splits (more only adds partial traffic).  Tiled kernel: aim for
+// 512 workgroups with at least 256 k per split.
+static void split_plan(int M, int N, int K, int dtype, int &splits, int &kc) {
+  splits = 1;
+  kc = K;
+  if (dtype == 0) return;
+  const bool sk = use_skinny(M, K);
+  const int bm = bm_for(M, K), bn = gemm_bn(M, dtype);
+  const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int unit = sk ? SK_KA : 64;  // split lengths are whole stages / K steps
+  int want, max_splits;
+  if (sk) {
+    const long cap = (M <= 32 ? 3 : (M <= 48 ? 2 : 1)) * 256L;
+    want = (int)(cap / tiles);
+    max_splits = std::min(K / 512, 8);
+  } else {
+    want = tiles >= 512 ? 1 : (int)((512 + tiles - 1) / tiles);
+    max_splits = K / 256;
+  }
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  kc = ((K + want - 1) / want + unit - 1) / unit * unit;
+  splits = (K + kc - 1) / kc;
 }
 
 int gemm_num_splits(int M, int N, int K, int dtype) {
-  if (dtype == 0) return 1;
-  const int bm = gemm_bm(M, dtype), bn = gemm_bn(M, dtype);
-  const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int target = 512;
-  if (tiles >= target) return 1;
-  int want = (int)((target + tiles - 1) / tiles);
-  const int max_splits = K / 256 > 0 ? K / 256 : 1;
-  if (want > max_splits) want = max_splits;
-  if (want < 1) want = 1;
-  // K per split rounded up to the 64-wide K step; recompute the count that covers K.
-  const int kc = ((K + want - 1) / want + 63) / 64 * 64;
-  return (K + kc - 1) / kc;
+  int splits, kc;
+  split_plan(M, N, K, dtype, splits, kc);
+  return splits;
 }
 
-hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st) {
+int gemm_kind(int M, int K, int dtype) {
+  if (dtype == 0) return 0;
+  return use_skinny(M, K) ? 1 : 2;
+}
+
+hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *splits_out,
+                       hipEvent_t ev_begin, hipEvent_t ev_end) {
   GemmArgs a = a0;
+  if (splits_out) *splits_out = 1;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  hipError_t e;
+  if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
   if (dtype == 0) {
     a.k_split = a.K;
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(NT), 0, st, a);
+    if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     return hipGetLastError();
   }
-  const int bm = gemm_bm(a.M, dtype), bn = gemm_bn(a.M, dtype);
-  const int splits = gemm_num_splits(a.M, a.N, a.K, dtype);
-  a.k_split = ((a.K + splits - 1) / splits + 63) / 64 * 64;
+  const int bm = bm_for(a.M, a.K), bn = gemm_bn(a.M, dtype);
+  int splits, kc;
+  split_plan(a.M, a.N, a.K, dtype, splits, kc);
+  a.k_split = kc;
+  if (splits_out) *splits_out = splits;
   dim3 grid((a.N + bn - 1) / bn, (a.M + bm - 1) / bm, splits);
-  if (bm == 32)
-    hipLaunchKernelGGL((gemm_mfma_kernel<32, 128, 1, 4>), grid, dim3(NT), 0, st, a);
-  else if (bm == 64)
-    hipLaunchKernelGGL((gemm_mfma_kernel<64, 128, 2, 2>), grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), grid, dim3(NT), 0, st, a);
+  switch (bm) {
+    case 16: hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(NT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(NT), 0, st, a); break;
+    case 48: hipLaunchKernelGGL(gemm_skinny_kernel<3>, grid, dim3(NT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(NT), 0, st, a); break;
+    default: hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), grid, dim3(NT), 0, st, a);
+  }
+  if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+  if (splits > 1 && a.epi != EPI_RESID) {
+    static_assert(RD_BN == SK_BN, "reduce tiles must match the GEMM's column tiles");
+    dim3 rgrid((a.N + RD_BN - 1) / RD_BN, (a.M + RD_BM - 1) / RD_BM);
+    hipLaunchKernelGGL(gemm_reduce_kernel, rgrid, dim3(NT), 0, st, a, splits);
+  }
   return hipGetLastError();
 }
 

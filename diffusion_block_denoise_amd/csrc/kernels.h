@@ -39,12 +39,14 @@ struct HeadPart {
 };
 
 struct GemmArgs {
-  // A operand: M x K, row-major with leading dimension lda.
+  // A operand: M x K, row-major with leading dimension lda; row m of A is row
+  // (m / row_per) * row_stride + row_off + m % row_per of the array (row_per 0: row m).
   //   bf16 path: a_hi + a_lo (two bf16 arrays whose sum is the fp32 activation)
   //   f32 path : a_f32
   const bf16 *a_hi, *a_lo;
   const float *a_f32;
   int lda;
+  int row_per, row_stride, row_off;
   // W operand: N x K rows from up to three segments (torch Linear layout, ld = K).
   // Plain mode: virtual row n lives in segment s with seg_end[s-1] <= n < seg_end[s].
   // SwiGLU mode: tile t, column c < BN/2 -> gate row t*BN/2 + c; else up row t*BN/2 + c - BN/2,
@@ -55,7 +57,6 @@ struct GemmArgs {
   int M, N, K;    // N is the virtual width (SwiGLU: 2 * ceil(ffn_dim / (BN/2)) * (BN/2))
   int k_split;    // K elements per split (multiple of the kernel's BK); gridDim.z splits
   float *partial; // split-K partial tiles [splits][M][N] fp32 (when gridDim.z > 1)
-  int *counters;  // per-tile arrival counters (zero between launches)
   int epi;
   // epilogue operands
   float *out_f32; int ld_out; float scale;        // STORE
@@ -63,8 +64,10 @@ struct GemmArgs {
   // QKV
   RowSet rows; int n_heads, n_kv_heads, head_dim;
   const float *rope_cos, *rope_sin;               // [L][head_dim/2]
-  void *q_out;                                    // [M][n_heads*head_dim] in storage type
-  void *k_cache, *vt_cache;                       // this layer: [B][Hkv][Lp][hd] and [B][Hkv][hd][Lp]
+  // q [M][n_heads*head_dim]; this layer's K [B][Hkv][Lp][hd] and transposed V [B][Hkv][hd][Lp].
+  // f32 path: one fp32 array each.  bf16 path: a hi and a lo bf16 plane each (hi + lo = value).
+  void *q_out, *q_out_lo;
+  void *k_cache, *k_cache_lo, *vt_cache, *vt_cache_lo;
   // SWIGLU output (bf16 path: hi/lo; f32 path: f32), ld = ld_act
   bf16 *act_hi, *act_lo; float *act_f32; int ld_act;
   // LMHEAD
@@ -72,25 +75,33 @@ struct GemmArgs {
 };
 
 // Storage-type tag for templates: 0 = f32, 1 = bf16.
-hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t st);
+// splits_out (may be NULL) receives the split-K count.  With EPI_RESID and more than one split
+// the GEMM only writes partial[split][M][N]; the caller folds them in with launch_resid_norm.
+// ev_begin/ev_end (may be NULL): recorded on st right before and after the main GEMM kernel.
+hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t st, int *splits_out,
+                       hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+// Which kernel launch_gemm uses: 0 = f32 SIMT, 1 = skinny weight-streaming, 2 = tiled MFMA.
+int gemm_kind(int M, int K, int dtype);
 // Tile width (N direction) that launch_gemm uses for a given M and dtype; SwiGLU and
 // the lm_head partial layout depend on it.
 int gemm_bn(int M, int dtype);
-int gemm_bm(int M, int dtype);
 int gemm_num_splits(int M, int N, int K, int dtype);
 
-// h[m] = embed[x[b][p]] (fp32); a = rmsnorm(h) * g written as hi/lo (bf16) or f32.
+// h[m] = embed[x[b][p]] (fp32); a = RMSNorm(h[m]) * gain as hi/lo planes (bf16) or f32.
 hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rows, int d,
                              float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
                              hipStream_t st);
-// a[i] = rmsnorm(h[row_of(i)]) * g for n rows; row_of(i) = (i / per) * stride + off + i % per.
-hipError_t launch_rmsnorm(const float *h, const void *gain, int n, int per, int stride, int off,
-                          int d, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
-                          hipStream_t st);
+// Per row m < M: h[m] += sum over the splits of partial[z][m] (in split order; splits 0: no
+// partials), then a[m] = RMSNorm(h[m]) * gain as hi/lo planes (bf16) or f32.
+hipError_t launch_resid_norm(int M, int d, float *h, const float *partial, int splits,
+                             const void *gain, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32,
+                             int dtype, hipStream_t st);
 // Non-causal attention of the rows' queries over all L cached positions.
-hipError_t launch_attention(const void *q, const void *k_cache, const void *vt_cache, RowSet rows,
-                            int n_heads, int n_kv_heads, int head_dim, bf16 *o_hi, bf16 *o_lo,
-                            float *o_f32, float *part, int dtype, hipStream_t st);
+// bf16 path: q, K and V^T come as hi/lo plane pairs; f32 path: the *_lo pointers are unused.
+hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache,
+                            const void *k_cache_lo, const void *vt_cache, const void *vt_cache_lo,
+                            RowSet rows, int n_heads, int n_kv_heads, int head_dim, bf16 *o_hi,
+                            bf16 *o_lo, float *o_f32, float *part, int dtype, hipStream_t st);
 size_t attention_part_bytes(RowSet rows, int n_heads, int n_kv_heads, int head_dim, int dtype);
 // Merge lm_head partials: tok, conf = 1/Z, p2 = exp(m2 - m1)/Z per row.
 hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,

@@ -1,6 +1,6 @@
-// Row-wise and bookkeeping kernels: embedding gather fused with RMSNorm, RMSNorm, the merge of
-// the fused lm_head's per-tile softmax partials, the commit rule, token-state initialisation,
-// the rotary table, and fills.
+// Row-wise and bookkeeping kernels: embedding gather + RMSNorm, split-K residual add + RMSNorm,
+// the merge of the fused lm_head's per-tile softmax partials, the commit rule, token-state
+// initialisation, the rotary table, and fills.
 #include "kernels.h"
 
 #include <limits.h>
@@ -12,7 +12,7 @@ template <> __device__ inline float ld_f<float>(const float *p, size_t i) { retu
 template <> __device__ inline float ld_f<bf16>(const bf16 *p, size_t i) { return __bfloat162float(p[i]); }
 
 __device__ inline float block_sum(float v) {
-  __shared__ float red[4];
+  __shared__ float red[16];
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
@@ -24,73 +24,121 @@ __device__ inline float block_sum(float v) {
   return s;
 }
 
-// One 256-thread workgroup per row: a = h * rsqrt(mean(h^2) + eps) * g.
+// a[i..i+3] = v * r * gain[i..i+3] as hi/lo bf16 planes or fp32.
 template <typename T>
-__device__ void norm_row(const float *hr, const T *gain, int d, float eps, size_t out_off,
-                         bf16 *a_hi, bf16 *a_lo, float *a_f32) {
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += hr[i] * hr[i];
-  ss = block_sum(ss);
-  const float r = rsqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    const float v = hr[i] * r * ld_f<T>(gain, i);
-    if (a_f32) {
-      a_f32[out_off + i] = v;
-    } else {
-      const bf16 hi = __float2bfloat16(v);
-      a_hi[out_off + i] = hi;
-      a_lo[out_off + i] = __float2bfloat16(v - __bfloat162float(hi));
-    }
+__device__ inline void norm_store4(float4 v, float r, const T *gain, size_t o, int i, bf16 *a_hi,
+                                   bf16 *a_lo, float *a_f32) {
+  const float x[4] = {v.x * r * ld_f<T>(gain, i), v.y * r * ld_f<T>(gain, i + 1),
+                      v.z * r * ld_f<T>(gain, i + 2), v.w * r * ld_f<T>(gain, i + 3)};
+  if (a_f32) {
+    *(float4 *)(a_f32 + o) = make_float4(x[0], x[1], x[2], x[3]);
+    return;
   }
+  uint32_t hw[2], lw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16 h0 = __float2bfloat16(x[2 * j]), h1 = __float2bfloat16(x[2 * j + 1]);
+    const bf16 l0 = __float2bfloat16(x[2 * j] - __bfloat162float(h0));
+    const bf16 l1 = __float2bfloat16(x[2 * j + 1] - __bfloat162float(h1));
+    hw[j] = (uint32_t)__bfloat16_as_ushort(h0) | ((uint32_t)__bfloat16_as_ushort(h1) << 16);
+    lw[j] = (uint32_t)__bfloat16_as_ushort(l0) | ((uint32_t)__bfloat16_as_ushort(l1) << 16);
+  }
+  *(uint2 *)(a_hi + o) = make_uint2(hw[0], hw[1]);
+  *(uint2 *)(a_lo + o) = make_uint2(lw[0], lw[1]);
 }
 
+// One workgroup of RN_NT threads per row; each thread keeps up to RN_MAX_C float4 chunks of the
+// row in registers (d <= RN_NT * 4 * RN_MAX_C = 8192).
+static constexpr int RN_NT = 1024, RN_MAX_C = 2;
+
+// One workgroup per row: h = embed[token], then a = RMSNorm(h) * gain.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int *x, const T *embed,
-                                                         const T *gain, RowSet rs, int d, float eps,
-                                                         float *h, bf16 *a_hi, bf16 *a_lo,
-                                                         float *a_f32) {
+__global__ __launch_bounds__(RN_NT) void embed_norm_kernel(const int *x, const T *embed,
+                                                           const T *gain, RowSet rs, int d,
+                                                           float eps, float *h, bf16 *a_hi,
+                                                           bf16 *a_lo, float *a_f32) {
   const int m = blockIdx.x;
   const int b = m / rs.nR, p = rs.start + m % rs.nR;
   const int tok = x[(size_t)b * rs.L + p];
-  float *hr = h + (size_t)m * d;
   const T *er = embed + (size_t)tok * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) hr[i] = ld_f<T>(er, i);
-  __syncthreads();
-  norm_row<T>(hr, gain, d, eps, (size_t)m * d, a_hi, a_lo, a_f32);
+  float4 v[RN_MAX_C];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < RN_MAX_C; ++c) {
+    const int i = (c * RN_NT + threadIdx.x) * 4;
+    if (i < d) {
+      v[c] = make_float4(ld_f<T>(er, i), ld_f<T>(er, i + 1), ld_f<T>(er, i + 2), ld_f<T>(er, i + 3));
+      *(float4 *)(h + (size_t)m * d + i) = v[c];
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+  }
+  const float r = rsqrtf(block_sum(ss) / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < RN_MAX_C; ++c) {
+    const int i = (c * RN_NT + threadIdx.x) * 4;
+    if (i < d) norm_store4<T>(v[c], r, gain, (size_t)m * d + i, i, a_hi, a_lo, a_f32);
+  }
 }
 
+// One workgroup per row: h += sum_z partial[z] (split order), a = RMSNorm(h) * gain.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *h, const T *gain, int per,
-                                                      int stride, int off, int d, float eps,
-                                                      bf16 *a_hi, bf16 *a_lo, float *a_f32) {
-  const int i = blockIdx.x;
-  const int row = (i / per) * stride + off + i % per;
-  norm_row<T>(h + (size_t)row * d, gain, d, eps, (size_t)i * d, a_hi, a_lo, a_f32);
+__global__ __launch_bounds__(RN_NT) void resid_norm_kernel(int M, int d, float *h,
+                                                           const float *__restrict__ part,
+                                                           int splits, const T *gain, float eps,
+                                                           bf16 *a_hi, bf16 *a_lo, float *a_f32) {
+  const int m = blockIdx.x;
+  const size_t MD = (size_t)M * d;
+  float4 v[RN_MAX_C];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < RN_MAX_C; ++c) {
+    const int i = (c * RN_NT + threadIdx.x) * 4;
+    if (i < d) {
+      const size_t o = (size_t)m * d + i;
+      float4 acc = *(const float4 *)(h + o);
+#pragma unroll 8
+      for (int z = 0; z < splits; ++z) {
+        const float4 q = *(const float4 *)(part + z * MD + o);
+        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+      }
+      v[c] = acc;
+      if (splits) *(float4 *)(h + o) = acc;
+      ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+    }
+  }
+  const float r = rsqrtf(block_sum(ss) / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < RN_MAX_C; ++c) {
+    const int i = (c * RN_NT + threadIdx.x) * 4;
+    if (i < d) norm_store4<T>(v[c], r, gain, (size_t)m * d + i, i, a_hi, a_lo, a_f32);
+  }
 }
 
 hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rs, int d,
                              float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
                              hipStream_t st) {
   if (rs.M() <= 0) return hipSuccess;
+  if (d % 4 || d > RN_NT * 4 * RN_MAX_C) return hipErrorInvalidValue;
   if (dtype == 0)
-    hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(rs.M()), dim3(256), 0, st, x,
+    hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(rs.M()), dim3(RN_NT), 0, st, x,
                        (const float *)embed, (const float *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
   else
-    hipLaunchKernelGGL(embed_norm_kernel<bf16>, dim3(rs.M()), dim3(256), 0, st, x,
+    hipLaunchKernelGGL(embed_norm_kernel<bf16>, dim3(rs.M()), dim3(RN_NT), 0, st, x,
                        (const bf16 *)embed, (const bf16 *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float *h, const void *gain, int n, int per, int stride, int off,
-                          int d, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
-                          hipStream_t st) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_resid_norm(int M, int d, float *h, const float *partial, int splits,
+                             const void *gain, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32,
+                             int dtype, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (d % 4 || d > RN_NT * 4 * RN_MAX_C) return hipErrorInvalidValue;
   if (dtype == 0)
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(n), dim3(256), 0, st, h, (const float *)gain,
-                       per, stride, off, d, eps, a_hi, a_lo, a_f32);
+    hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(M), dim3(RN_NT), 0, st, M, d, h, partial,
+                       splits, (const float *)gain, eps, a_hi, a_lo, a_f32);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(n), dim3(256), 0, st, h, (const bf16 *)gain, per,
-                       stride, off, d, eps, a_hi, a_lo, a_f32);
+    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(M), dim3(RN_NT), 0, st, M, d, h, partial,
+                       splits, (const bf16 *)gain, eps, a_hi, a_lo, a_f32);
   return hipGetLastError();
 }
 

@@ -52,6 +52,15 @@ class dllm_stats(C.Structure):
         return d
 
 
+DLLM_KC_GEMM_SKINNY, DLLM_KC_GEMM_TILED, DLLM_KC_ATTENTION, DLLM_KC_COUNT = 0, 1, 2, 3
+KC_NAMES = ["gemm_skinny", "gemm_tiled", "attention"]
+
+
+class dllm_kernel_prof(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("ms", C.c_double), ("bytes", C.c_double),
+                ("flops", C.c_double)]
+
+
 class DllmError(RuntimeError):
     def __init__(self, fn: str, code: int, msg: str):
         super().__init__(f"{fn} failed: {ERR_NAMES.get(code, code)}: {msg}")
@@ -76,6 +85,8 @@ _SIGS = {
     "dllm_debug_block_logits": (C.c_int, [_P, _P]),
     "dllm_get_stats": (C.c_int, [_P, C.POINTER(dllm_stats)]),
     "dllm_get_position": (C.c_int, [_P, _I32P, _I32P]),
+    "dllm_set_profiling": (C.c_int, [_P, C.c_int]),
+    "dllm_get_profile": (C.c_int, [_P, C.POINTER(dllm_kernel_prof)]),
     "dllm_last_error": (C.c_char_p, [_P]),
     "dllm_destroy": (None, [_P]),
 }
@@ -244,6 +255,15 @@ class Handle:
         b, j = C.c_int32(0), C.c_int32(0)
         self._check("dllm_get_position", self.lib.dllm_get_position(self.h, C.byref(b), C.byref(j)))
         return b.value, j.value
+
+    def set_profiling(self, class_mask: int) -> None:
+        self._check("dllm_set_profiling", self.lib.dllm_set_profiling(self.h, int(class_mask)))
+
+    def get_profile(self) -> dict:
+        arr = (dllm_kernel_prof * DLLM_KC_COUNT)()
+        self._check("dllm_get_profile", self.lib.dllm_get_profile(self.h, arr))
+        return {KC_NAMES[i]: dict(launches=arr[i].launches, ms=arr[i].ms, bytes=arr[i].bytes,
+                                  flops=arr[i].flops) for i in range(DLLM_KC_COUNT)}
 
     def destroy(self) -> None:
         if getattr(self, "h", None):

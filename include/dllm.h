@@ -206,6 +206,30 @@ int dllm_get_stats(dllm_t *h, dllm_stats *stats);
 /* Device-side phase of the handle for tests: current block, step index in it. */
 int dllm_get_position(dllm_t *h, int32_t *block, int32_t *step);
 
+/*
+ * Per-kernel-class timing, a measurement aid.  While enabled, every launch of a selected class
+ * is bracketed by HIP events on cfg.stream; durations are collected at the next synchronising
+ * call together with each launch's algorithmic work: bytes = every weight, activation and
+ * output element the launch must read or write once; flops = 2*M*N*K for a GEMM and
+ * 4*queries*keys*head_dim for attention.  Classes:
+ */
+#define DLLM_KC_GEMM_SKINNY 0 /* weight-streaming GEMM, <= 64 rows (cached steps, lm_head)     */
+#define DLLM_KC_GEMM_TILED 1  /* tiled MFMA GEMM, > 64 rows (block refresh, no-cache forward)   */
+#define DLLM_KC_ATTENTION 2   /* attention (with its split merge)                               */
+#define DLLM_KC_COUNT 3
+typedef struct dllm_kernel_prof {
+  int64_t launches;
+  double ms;     /* summed event-measured duration */
+  double bytes;  /* summed algorithmic bytes       */
+  double flops;  /* summed algorithmic flops       */
+} dllm_kernel_prof;
+
+/* Enable (mask bit 1 << class) or disable (0) timing, and clear the counters. */
+int dllm_set_profiling(dllm_t *h, int class_mask);
+
+/* Counters per class since dllm_set_profiling; out: host array of DLLM_KC_COUNT.  Synchronises. */
+int dllm_get_profile(dllm_t *h, dllm_kernel_prof *out);
+
 /* Message of the last error on h (or of the last failed dllm_create when h is NULL). */
 const char *dllm_last_error(const dllm_t *h);
 

@@ -61,14 +61,14 @@ def test_workloads_validate_and_size(name):
     cfg = synth.configs.get(name)
     L = cfg["prompt_len"] + cfg["gen_length"]
     Lp = (L + 31) // 32 * 32
-    esz = 2 if cfg["dtype"] == "bf16" else 4
-    kv = 2 * cfg["n_layers"] * cfg["batch"] * cfg["n_kv_heads"] * Lp * cfg["head_dim"] * esz
+    # K and V: fp32, or bf16 hi + lo planes: 4 bytes per cached element either way
+    kv = 2 * cfg["n_layers"] * cfg["batch"] * cfg["n_kv_heads"] * Lp * cfg["head_dim"] * 4
     assert kv < n < kv + 40 * 2 ** 30
 
 
 def test_long_context_workspace_fits_one_gpu():
     n = dllm.dllm_workspace_bytes(dllm.make_cfg(synth.configs.get("llada8b_long")))
-    assert 43e9 < n < 200e9     # ~43 GB of KV cache plus activations, within 288 GB of HBM
+    assert 86e9 < n < 200e9     # ~86 GB of K/V (hi/lo pairs) plus activations, within 288 GB
 
 
 BAD = [

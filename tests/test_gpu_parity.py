@@ -166,3 +166,22 @@ def test_call_order_errors():
     with pytest.raises(dllm.DllmError) as e:
         h.prefill(bad)
     assert e.value.code == dllm.DLLM_EINVAL
+
+
+def test_profiling_counts_launches():
+    from diffusion_block_denoise_amd import dllm
+    cfg = small_bf16(batch=5, block_size=32, gen_length=64)   # M = 160: tiled GEMM at refresh
+    h = _handle(cfg)
+    h.set_profiling((1 << dllm.DLLM_KC_COUNT) - 1)
+    _, st = h.generate(synth.prompt_np(cfg))
+    prof = h.get_profile()
+    L = cfg["n_layers"]
+    fwd = st["full_forwards"] + st["cached_forwards"]
+    assert prof["attention"]["launches"] == L * fwd
+    # 4 GEMMs per layer and the lm_head per forward; every row count here is above 64
+    assert prof["gemm_tiled"]["launches"] == (4 * L + 1) * fwd
+    assert prof["gemm_skinny"]["launches"] == 0
+    for k in ("attention", "gemm_tiled"):
+        assert prof[k]["ms"] > 0 and prof[k]["bytes"] > 0 and prof[k]["flops"] > 0
+    h.set_profiling(0)
+    assert h.get_profile()["attention"]["launches"] == 0
