@@ -184,6 +184,171 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   }
 }
 
+// Many-query variant (block refresh): 4 waves per workgroup, one 32-query tile each, all of the
+// same (batch row, K/V head).  The 32-key tiles of K and V^T (hi and lo) are staged once per
+// workgroup in LDS, double-buffered with one barrier per tile, the next tile prefetched into
+// registers while the current one is used; every wave then runs the same MFMA sequence as the
+// per-wave kernel with its operands read from LDS.
+static constexpr int AW_WAVES = 4;
+
+template <int HD>
+__global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
+    const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
+    const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
+    RowSet rs, int H, int Hkv, float scale_log2, bf16 *o_hi, bf16 *o_lo) {
+  constexpr int KS = HD / 16, DB = HD / 32;
+  constexpr int KP = HD + 8;   // K tile row pitch (keys x dims), bf16 elements
+  constexpr int VP = 32 + 8;   // V^T tile row pitch (dims x keys)
+  constexpr int K_ELEMS = 32 * KP, V_ELEMS = HD * VP;
+  constexpr int STAGE = 2 * K_ELEMS + 2 * V_ELEMS;  // hi and lo of each
+  // 16-byte chunks per stage: K hi/lo 32*HD/8 each, V^T hi/lo HD*32/8 each
+  constexpr int CHUNKS = 4 * (32 * HD / 8);
+  constexpr int NTH = 64 * AW_WAVES;
+  constexpr int CPT = CHUNKS / NTH;  // chunks per thread
+  static_assert(CHUNKS % NTH == 0, "tile staging");
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  __shared__ __align__(16) uint16_t lds[2 * STAGE];
+
+  const int G = H / Hkv;
+  const int nrows = rs.nR * G;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int qt = blockIdx.x * AW_WAVES + wave;
+  const int r = qt * 32 + col;
+  const bool valid = r < nrows;
+  const int pi = valid ? r / G : 0;
+  const int head = g * G + (valid ? r % G : 0);
+  const int m = b * rs.nR + pi;
+  const int ldq = H * HD;
+
+  bf16x8_t qh[KS], ql[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const size_t o = (size_t)m * ldq + head * HD + kk * 16 + half * 8;
+    qh[kk] = *(const bf16x8_t *)(q_hi + o);  // invalid rows read row m of batch b: harmless
+    ql[kk] = *(const bf16x8_t *)(q_lo + o);
+  }
+  const size_t kv_off = (size_t)bg * rs.Lp * HD;
+  const uint16_t *src[4] = {(const uint16_t *)k_hi + kv_off, (const uint16_t *)k_lo + kv_off,
+                            (const uint16_t *)vt_hi + kv_off, (const uint16_t *)vt_lo + kv_off};
+
+  // chunk c of a stage: plane = c / (32*HD/8); K planes: key c' / (HD/8), dims 8*(c' % (HD/8));
+  // V^T planes: dim c' / 4, keys 8*(c' % 4)
+  s16x8 pre[CPT];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NTH, plane = c / (32 * HD / 8), cc = c % (32 * HD / 8);
+      size_t off;
+      if (plane < 2) off = (size_t)(kb + cc / (HD / 8)) * HD + 8 * (cc % (HD / 8));
+      else off = (size_t)(cc / 4) * rs.Lp + kb + 8 * (cc % 4);
+      pre[i] = *(const s16x8 *)(src[plane] + off);
+    }
+  };
+  auto store_tile = [&](uint16_t *st) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NTH, plane = c / (32 * HD / 8), cc = c % (32 * HD / 8);
+      uint16_t *dst;
+      if (plane < 2) dst = st + plane * K_ELEMS + (cc / (HD / 8)) * KP + 8 * (cc % (HD / 8));
+      else dst = st + 2 * K_ELEMS + (plane - 2) * V_ELEMS + (cc / 4) * VP + 8 * (cc % 4);
+      *(s16x8 *)dst = pre[i];
+    }
+  };
+
+  float mrun = -INFINITY, lsum = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+
+  const int ntile = rs.Lp / 32;
+  load_tile(0);
+  store_tile(lds);
+  load_tile(min(1, ntile - 1) * 32);
+  for (int t = 0; t < ntile; ++t) {
+    __syncthreads();  // tile t in lds[t&1]; everyone is done with lds[(t+1)&1]
+    uint16_t *cur = lds + (t & 1) * STAGE;
+    if (t + 1 < ntile) store_tile(lds + ((t + 1) & 1) * STAGE);
+    load_tile(min(t + 2, ntile - 1) * 32);  // clamped: unconditional loads keep counts static
+    const int kb = t * 32;
+    const uint16_t *Kh = cur, *Kl = cur + K_ELEMS;
+    const uint16_t *Vh = cur + 2 * K_ELEMS, *Vl = Vh + V_ELEMS;
+    f32x16 sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const bf16x8_t kh = *(const bf16x8_t *)(Kh + col * KP + kk * 16 + half * 8);
+      const bf16x8_t kl = *(const bf16x8_t *)(Kl + col * KP + kk * 16 + half * 8);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kk], sc, 0, 0, 0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+      sc[i] = key < rs.L ? sc[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+    bf16x8_t ph[2], pl[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = exp2f(sc[i] - mnew);
+      const __bf16 hi = (__bf16)pv;
+      ph[i >> 3][i & 7] = hi;
+      pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
+      psum += pv;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    lsum = lsum * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      const int vrow = (d * 32 + col) * VP + 4 * half;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x4_t h0 = *(const bf16x4_t *)(Vh + vrow + 16 * ks);
+        const bf16x4_t h1 = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8);
+        const bf16x4_t l0 = *(const bf16x4_t *)(Vl + vrow + 16 * ks);
+        const bf16x4_t l1 = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8);
+        bf16x8_t vh, vl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vh[e] = h0[e]; vh[e + 4] = h1[e];
+          vl[e] = l0[e]; vl[e + 4] = l1[e];
+        }
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl[ks], o[d], 0, 0, 0);
+      }
+    }
+  }
+  if (!valid) return;
+  const float inv = 1.0f / lsum;
+  bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
+  bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      const float v = o[d][i] * inv;
+      const bf16 hi = __float2bfloat16(v);
+      oh[dim] = hi;
+      ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+    }
+}
+
 // Combine the key chunks: one wave per query row slot, lanes over dims.
 template <int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict__ part, RowSet rs,
@@ -271,11 +436,31 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
                        Hkv, hd, 1.0f / sqrtf((float)hd), o_f32);
     return hipGetLastError();
   }
+  const int nqt = attn_tiles(rs, H, Hkv);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
+  if (nqt >= AW_WAVES) {
+    // many queries: K/V tiles shared by the 4 waves of a workgroup through LDS
+    dim3 wgrid((nqt + AW_WAVES - 1) / AW_WAVES, rs.B * Hkv);
+#define ATTNW_CASE(HDV)                                                                          \
+  case HDV:                                                                                      \
+    hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES), 0, st, (const bf16 *)q, \
+                       (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,      \
+                       (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv,            \
+                       scale_log2, o_hi, o_lo);                                                  \
+    break;
+    switch (hd) {
+      ATTNW_CASE(32)
+      ATTNW_CASE(64)
+      ATTNW_CASE(128)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef ATTNW_CASE
+    return hipGetLastError();
+  }
   int splits, chunk;
   attn_plan(rs, H, Hkv, splits, chunk);
-  const int nqt = attn_tiles(rs, H, Hkv);
   dim3 grid(nqt, rs.B * Hkv, splits);
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
 #define ATTN_CASE(HDV)                                                                          \
   case HDV:                                                                                     \
     hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \

@@ -529,8 +529,7 @@ static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16)
 
 // Split-K plan.  Skinny kernel: as many splits as keep the grid within one round of resident
 // workgroups (3 per CU up to 32 rows, 2 up to 48, 1 at 64), at least 512 k per split and at
-// most 8 splits (more only adds partial traffic).  Tiled kernel: aim for
-// 512 workgroups with at least 256 k per split.
+// most 8 splits (more only adds partial traffic).  Tiled kernel: see below.
 static void split_plan(int M, int N, int K, int dtype, int &splits, int &kc) {
   splits = 1;
   kc = K;
@@ -545,8 +544,18 @@ static void split_plan(int M, int N, int K, int dtype, int &splits, int &kc) {
     want = (int)(cap / tiles);
     max_splits = std::min(K / 512, 8);
   } else {
-    want = tiles >= 512 ? 1 : (int)((512 + tiles - 1) / tiles);
-    max_splits = K / 256;
+    // Rounds of resident workgroups (2 per CU) times K steps per split, plus 6% per extra split
+    // for the partial traffic and the reduce; at most 16 splits of at least 4 K steps.
+    const int iters = K / 64;
+    const long slots = 512;
+    double best = 1e30;
+    want = 1;
+    for (int sp = 1; sp <= 16 && sp <= std::max(1, iters / 4); ++sp) {
+      const long rounds = (tiles * sp + slots - 1) / slots;
+      const double cost = (double)rounds * ((iters + sp - 1) / sp) * (1.0 + 0.06 * (sp - 1));
+      if (cost < best - 1e-9) { best = cost; want = sp; }
+    }
+    max_splits = std::max(1, K / 256);
   }
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
