@@ -89,7 +89,10 @@ struct Plan {
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
-      off_ncom, off_rem, total;
+      off_ncom, off_rem, off_wpack, total;
+  // packed bf16 weights (elements): per layer QKV, Wo, gate/up, down, then the lm_head
+  int n_gu;  // virtual gate/up width (64 gate + 64 up rows per 128-row panel)
+  size_t wp_qkv, wp_o, wp_gu, wp_down, wp_layer, wp_lm;
   size_t kv_layer_elems;  // K (or V) elements per layer
   int n_vtiles;
 };
@@ -136,8 +139,18 @@ void make_plan(const dllm_cfg *c, Plan &p) {
     if (splits > 1) gpart = std::max(gpart, (size_t)splits * M * p.V * sizeof(float));
   }
 
+  // packed copies of the bf16 linear weights (the GEMM W layout)
+  p.n_gu = 2 * ((p.F + 63) / 64) * 64;
+  p.wp_qkv = packed_rows(p.nq + 2 * p.nkv) * p.d;
+  p.wp_o = packed_rows(p.d) * p.nq;
+  p.wp_gu = packed_rows(p.n_gu) * p.d;
+  p.wp_down = packed_rows(p.d) * p.F;
+  p.wp_layer = p.wp_qkv + p.wp_o + p.wp_gu + p.wp_down;
+  p.wp_lm = packed_rows(p.V) * p.d;
+
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  p.off_wpack = take(p.dt ? (p.wp_layer * c->n_layers + p.wp_lm) * 2 : 0);
   p.off_x = take(Mmax * 4);
   // K and V^T caches, per layer: fp32, or a bf16 hi plane followed by a bf16 lo plane
   p.off_k = take(p.kv_layer_elems * c->n_layers * 4);
@@ -176,6 +189,7 @@ struct dllm_handle {
   std::vector<const void *> layer;
   char *ws;
   // carved buffers
+  uint16_t *wpack;  // packed bf16 weights
   int *x;
   char *kc, *vc;
   float *cos_t, *sin_t, *h;
@@ -223,6 +237,16 @@ namespace {
   } while (0)
 
 inline const void *LW(dllm_t *h, int l, int j) { return h->layer[(size_t)9 * l + j]; }
+
+// Packed bf16 weight of layer l: j = 0 QKV, 1 Wo, 2 gate/up, 3 down; l = n_layers: the lm_head.
+const uint16_t *WP(dllm_t *h, int l, int j) {
+  const Plan &p = h->p;
+  if (!p.dt) return nullptr;
+  const uint16_t *b = h->wpack + p.wp_layer * l;
+  if (l == h->cfg.n_layers) return b;
+  const size_t off[4] = {0, p.wp_qkv, p.wp_qkv + p.wp_o, p.wp_qkv + p.wp_o + p.wp_gu};
+  return b + off[j];
+}
 
 // ---- per-kernel-class timing -------------------------------------------------------------------
 // Collect the durations of the pending event pairs (the stream has been synchronised).
@@ -347,6 +371,7 @@ int forward(dllm_t *h, RowSet rs) {
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.nq + 2 * p.nkv, p.d);
       g.w[0] = LW(h, l, 1); g.w[1] = LW(h, l, 2); g.w[2] = LW(h, l, 3);
       g.seg_end[0] = p.nq; g.seg_end[1] = p.nq + p.nkv; g.seg_end[2] = p.nq + 2 * p.nkv;
+      g.wp = WP(h, l, 0);
       g.epi = EPI_QKV;
       g.rows = rs; g.n_heads = p.H; g.n_kv_heads = p.Hkv; g.head_dim = p.hd;
       g.rope_cos = h->cos_t; g.rope_sin = h->sin_t;
@@ -384,6 +409,7 @@ int forward(dllm_t *h, RowSet rs) {
     {
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.nq, M, p.d, p.nq);
       g.w[0] = LW(h, l, 4); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
+      g.wp = WP(h, l, 1);
       set_resid(h, g);
       int rc = resid_gemm_norm(h, g, LW(h, l, 5));
       if (rc) return rc;
@@ -394,6 +420,7 @@ int forward(dllm_t *h, RowSet rs) {
       const int nvirt = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, nvirt, p.d);
       g.w[0] = LW(h, l, 6); g.w[1] = LW(h, l, 7);
+      g.wp = WP(h, l, 2);
       g.n_half = p.F;
       g.epi = EPI_SWIGLU;
       g.ld_act = p.F;
@@ -406,6 +433,7 @@ int forward(dllm_t *h, RowSet rs) {
     {
       GemmArgs g = gemm_base(h, h->act_hi, h->act_lo, p.F, M, p.d, p.F);
       g.w[0] = LW(h, l, 8); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
+      g.wp = WP(h, l, 3);
       set_resid(h, g);
       int rc = resid_gemm_norm(h, g, l + 1 < c.n_layers ? LW(h, l + 1, 0) : h->final_norm);
       if (rc) return rc;
@@ -432,6 +460,7 @@ int head(dllm_t *h) {
   GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
   set_block_rows(h, g);
   g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
+  g.wp = WP(h, h->cfg.n_layers, 0);
   g.epi = EPI_LMHEAD;
   g.scale = h->cfg.logit_scale;
   g.head_part = h->hpart; g.n_vtiles = p.n_vtiles; g.vocab = p.V; g.mask_id = h->cfg.mask_id;
@@ -575,6 +604,7 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->layer.assign(w->layer, w->layer + 9 * cfg->n_layers);
   char *ws = (char *)workspace;
   h->ws = ws;
+  h->wpack = (uint16_t *)(ws + p.off_wpack);
   h->x = (int *)(ws + p.off_x);
   h->kc = ws + p.off_k; h->vc = ws + p.off_v;
   h->cos_t = (float *)(ws + p.off_cos); h->sin_t = (float *)(ws + p.off_sin);
@@ -602,6 +632,32 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
     return fail(e, "zero cache");
   if ((e = launch_rope_table(h->cos_t, h->sin_t, p.L, p.hd, cfg->rope_base, h->st)) != hipSuccess)
     return fail(e, "rope table");
+  // Packed copies of the bf16 linear weights; the originals are not read again.
+  if (p.dt) {
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const void *qkv[3] = {LW(h, l, 1), LW(h, l, 2), LW(h, l, 3)};
+      const int qkv_end[3] = {p.nq, p.nq + p.nkv, p.nq + 2 * p.nkv};
+      const void *o[3] = {LW(h, l, 4), nullptr, nullptr};
+      const int o_end[3] = {p.d, p.d, p.d};
+      const void *gu[3] = {LW(h, l, 6), LW(h, l, 7), nullptr};
+      const int gu_end[3] = {p.n_gu, p.n_gu, p.n_gu};
+      const void *dn[3] = {LW(h, l, 8), nullptr, nullptr};
+      if ((e = launch_pack_weight((uint16_t *)WP(h, l, 0), qkv, qkv_end, 0, PACK_CONCAT, p.nq + 2 * p.nkv,
+                                  p.d, h->st)) != hipSuccess ||
+          (e = launch_pack_weight((uint16_t *)WP(h, l, 1), o, o_end, 0, PACK_PLAIN, p.d, p.nq, h->st)) !=
+              hipSuccess ||
+          (e = launch_pack_weight((uint16_t *)WP(h, l, 2), gu, gu_end, p.F, PACK_SWIGLU, p.n_gu, p.d,
+                                  h->st)) != hipSuccess ||
+          (e = launch_pack_weight((uint16_t *)WP(h, l, 3), dn, o_end, 0, PACK_PLAIN, p.d, p.F, h->st)) !=
+              hipSuccess)
+        return fail(e, "pack weights");
+    }
+    const void *lm[3] = {h->lm_head, nullptr, nullptr};
+    const int lm_end[3] = {p.V, p.V, p.V};
+    if ((e = launch_pack_weight((uint16_t *)WP(h, cfg->n_layers, 0), lm, lm_end, 0, PACK_PLAIN, p.V, p.d,
+                                h->st)) != hipSuccess)
+      return fail(e, "pack lm_head");
+  }
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return fail(e, "synchronize");
   *out = h;
   return DLLM_OK;
@@ -698,6 +754,7 @@ int dllm_debug_block_logits(dllm_t *h, float *logits_dev) {
   GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.V, p.d);
   set_block_rows(h, g);
   g.w[0] = h->lm_head; g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = p.V;
+  g.wp = WP(h, h->cfg.n_layers, 0);
   g.epi = EPI_STORE; g.out_f32 = logits_dev; g.ld_out = p.V; g.scale = h->cfg.logit_scale;
   HIPCHK(launch_gemm(g, p.dt, h->st, nullptr));
   HIPCHK(launch_mask_column(logits_dev, M, p.V, h->cfg.mask_id, h->st));

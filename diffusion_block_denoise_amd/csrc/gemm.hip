@@ -53,6 +53,50 @@ __device__ inline int a_row(const GemmArgs &a, int m) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Packed W: start of panel p (128 rows), block kb (32 columns); row r of the block at r * 32.
+__device__ inline const uint16_t *wp_block(const GemmArgs &a, int p, int kb) {
+  return a.wp + ((size_t)p * (a.K / PW_K) + kb) * (PW_ROWS * PW_K);
+}
+
+// Pack kernel: one thread per 16-byte chunk of the packed matrix (coalesced writes).
+__global__ __launch_bounds__(256) void pack_weight_kernel(uint16_t *dst, const GemmArgs a, int mode,
+                                                          size_t chunks) {
+  const size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (q >= chunks) return;
+  const int kblocks = a.K / PW_K;
+  const size_t blk = q / (PW_ROWS * PW_K / 8);
+  const int within = (int)(q % (PW_ROWS * PW_K / 8));
+  const int p = (int)(blk / kblocks), kb = (int)(blk % kblocks);
+  const int r = within / (PW_K / 8), c8 = (within % (PW_K / 8)) * 8;
+  const int n = p * PW_ROWS + r, k = kb * PW_K + c8;
+  const uint16_t *src = nullptr;
+  if (mode == PACK_SWIGLU) {
+    const int c = r, f = p * 64 + (c < 64 ? c : c - 64);
+    if (f < a.n_half) src = (const uint16_t *)a.w[c < 64 ? 0 : 1] + (size_t)f * a.K;
+  } else if (n < a.N) {
+    int sgi = 0, base = 0;
+    if (mode == PACK_CONCAT)
+      while (sgi < 2 && n >= a.seg_end[sgi]) { base = a.seg_end[sgi]; ++sgi; }
+    src = (const uint16_t *)a.w[sgi] + (size_t)(n - base) * a.K;
+  }
+  s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (src) v = *(const s16x8 *)(src + k);
+  *(s16x8 *)(dst + q * 8) = v;
+}
+
+hipError_t launch_pack_weight(uint16_t *dst, const void *const src[3], const int seg_end[3],
+                              int n_half, int mode, int N, int K, hipStream_t st) {
+  if (N <= 0 || K <= 0 || K % PW_K) return hipErrorInvalidValue;
+  GemmArgs a{};
+  for (int i = 0; i < 3; ++i) { a.w[i] = src[i]; a.seg_end[i] = seg_end[i]; }
+  a.n_half = n_half; a.N = N; a.K = K;
+  const size_t chunks = packed_rows(N) * (size_t)K / 8;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, dst, a,
+                     mode, chunks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Epilogues over an fp32 C tile in LDS (ld = ldc).  T is the storage type of q and the cache.
 __device__ inline float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -250,11 +294,13 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
   constexpr int W_CH = BN * BK / 8 / NT;
   static_assert(A_CH >= 1 && W_CH >= 1, "tile too small");
   s16x8 ra_hi[A_CH], ra_lo[A_CH], rw[W_CH];
+  static_assert(BN == PW_ROWS && BK == 2 * PW_K, "one panel, two blocks per K step");
+  // packed W: chunk (row r, column c8) of K step k0 is in block k0/32 + c8/32 of panel n0/128
   const uint16_t *wrow[W_CH];
 #pragma unroll
   for (int i = 0; i < W_CH; ++i) {
-    const int ch = tid + i * NT, r = ch / 8;
-    wrow[i] = w_row<uint16_t>(a, BN, n0, r);
+    const int ch = tid + i * NT, r = ch / 8, c8 = (ch % 8) * 8;
+    wrow[i] = wp_block(a, n0 / PW_ROWS, c8 / PW_K) + r * PW_K + c8 % PW_K;
   }
   // A row offsets, hoisted out of the K loop (rows past M read row M-1; they only feed output
   // rows that are never written)
@@ -272,10 +318,7 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
       ra_lo[i] = *(const s16x8 *)((const uint16_t *)a.a_lo + aoff[i] + k0);
     }
 #pragma unroll
-    for (int i = 0; i < W_CH; ++i) {
-      const int ch = tid + i * NT, c8 = (ch % 8) * 8;
-      rw[i] = wrow[i] ? *(const s16x8 *)(wrow[i] + k0 + c8) : (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int i = 0; i < W_CH; ++i) rw[i] = *(const s16x8 *)(wrow[i] + (size_t)(k0 / PW_K) * (PW_ROWS * PW_K));
   };
   auto store = [&]() {
 #pragma unroll
@@ -353,6 +396,148 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Wide tiled bf16 MFMA kernel for many rows (block refresh).  128 x 256 tile, 4 waves as 2 x 2,
+// each wave 64 x 128 in 32x32 blocks (v_mfma_f32_32x32x16_bf16), BK = 32.
+//
+// Why this shape: per 16-wide K step a wave reads 2 A blocks (hi and lo) and 4 W blocks from
+// LDS for 16 MFMAs, 0.5 KB of LDS reads per MFMA instead of 0.75 KB for a 64 x 64 wave tile.
+// Tiles reach LDS by direct global->LDS loads (16 bytes per lane), so no staging registers and
+// no LDS write instructions; two stages alternate, and the loads of stage t+1 are issued right
+// after the fragments of stage t have been read, so they overlap stage t's MFMAs.
+//
+// LDS layout of a stage: A hi [128 rows][32 k], A lo [128][32], W [256][32], bf16.  A row is four
+// 16-byte chunks; chunk c of row r sits at position r*4 + (c ^ ((r >> 2) & 3)).  One load
+// instruction fills 64 consecutive positions, and a fragment read (16 lanes = 16 consecutive
+// rows, one chunk) hits 16 distinct 16-byte bank groups.
+static constexpr int WT_BM = 128, WT_BN = 256, WT_BK = 32;
+
+__device__ inline int wt_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(NT, 2) void gemm_wide_kernel(const GemmArgs a) {
+  constexpr int BM = WT_BM, BN = WT_BN, BK = WT_BK;
+  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2;
+  constexpr int STAGE = 2 * A_BYTES + W_BYTES;  // 32 KB
+  constexpr int LDC = 128 + 4;
+  constexpr int CT_BYTES = BM * LDC * 4;
+  constexpr int SMEM = 2 * STAGE > CT_BYTES ? 2 * STAGE : CT_BYTES;
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  float *Ct = (float *)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kbeg = blockIdx.z * a.k_split;
+  const int kend = min(a.K, kbeg + a.k_split);
+  const int T = (kend - kbeg) / BK;
+
+  // Per-lane sources of the direct loads.  A: instructions 2*wave + {0,1} of each plane, rows
+  // (slot >> 2); W: instructions 4*wave + {0..3}.  Rows past M read row M-1 and rows past N read
+  // row 0 of W: they only feed outputs that are never written.
+  size_t aoff[2];
+  int acol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = (2 * wave + i) * 64 + lane, r = slot >> 2;
+    aoff[i] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda;
+    acol[i] = ((slot & 3) ^ ((r >> 2) & 3)) * 8;
+  }
+  // W: packed panels n0/128 and n0/128 + 1 (the second clamped to the last panel; its columns
+  // are then past N and never written)
+  const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
+  const uint16_t *wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (4 * wave + i) * 64 + lane, r = slot >> 2;
+    wsrc[i] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K +
+              ((slot & 3) ^ ((r >> 2) & 3)) * 8;
+  }
+  auto issue = [&](int t, int buf) {
+    const int k0 = kbeg + t * BK;
+    unsigned char *st = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = 2 * wave + i;
+      __builtin_amdgcn_global_load_lds((const void *)((const uint16_t *)a.a_hi + aoff[i] + k0 + acol[i]),
+                                       (lds_void *)(st + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)((const uint16_t *)a.a_lo + aoff[i] + k0 + acol[i]),
+                                       (lds_void *)(st + A_BYTES + j * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * wave + i;
+      __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + (size_t)(k0 / PW_K) * (PW_ROWS * PW_K)),
+                                       (lds_void *)(st + 2 * A_BYTES + j * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int frow = lane & 31, fc = lane >> 5;
+  if (T > 0) issue(0, 0);
+  for (int t = 0; t < T; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage t have landed
+    __syncthreads();                      // ... and every wave's; stage t^1 is free again
+    const unsigned char *st = smem + (t & 1) * STAGE;
+    const uint16_t *Ah = (const uint16_t *)st, *Al = (const uint16_t *)(st + A_BYTES);
+    const uint16_t *Ws = (const uint16_t *)(st + 2 * A_BYTES);
+    bf16x8_t fa_hi[2][2], fa_lo[2][2], fb[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int p = wt_pos(wm * 64 + i * 32 + frow, kk * 2 + fc) * 8;
+        fa_hi[kk][i] = *(const bf16x8_t *)(Ah + p);
+        fa_lo[kk][i] = *(const bf16x8_t *)(Al + p);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[kk][j] = *(const bf16x8_t *)(Ws + wt_pos(wn * 128 + j * 32 + frow, kk * 2 + fc) * 8);
+    }
+    if (t + 1 < T) issue(t + 1, (t + 1) & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_hi[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_lo[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+        }
+  }
+  __syncthreads();
+  // Two 128-column halves through the C tile: the waves of half h write their accumulators, then
+  // the whole workgroup runs the epilogue of that 128 x 128 sub-tile.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wn == h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+            Ct[row * LDC + j * 32 + (lane & 31)] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    if (gridDim.z > 1)
+      write_partial<BM, 128>(a, Ct, LDC, m0, n0 + 128 * h);
+    else
+      run_epilogue<bf16, BM, 128>(a, Ct, LDC, m0, n0 + 128 * h);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Weight-streaming bf16 kernel for few rows (M <= 16*MT <= 64): the shape of a cached step, where
 // the time is the HBM read of W.  4 waves x 32 W rows = 128 columns per workgroup.
 //   W: each lane loads straight into the B-operand registers of v_mfma_f32_16x16x32_bf16 (lane:
@@ -389,20 +574,19 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
   const int nchunk = (kend - kbeg) / 64;
   const int nstage = (nchunk + SK_D - 1) / SK_D;
 
-  // W rows of this lane (a row past N reads row 0 of segment 0)
+  // W rows of this lane in the packed panel n0/128 (rows past N are zero-padded)
+  static_assert(SK_BN == PW_ROWS, "one panel per workgroup");
   const uint16_t *wr[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    wr[cb] = w_row<uint16_t>(a, SK_BN, n0, wave * 32 + cb * 16 + rn);
-    if (!wr[cb]) wr[cb] = (const uint16_t *)a.w[0];
-  }
+  for (int cb = 0; cb < 2; ++cb) wr[cb] = wp_block(a, n0 / PW_ROWS, 0) + (wave * 32 + cb * 16 + rn) * PW_K + 8 * g;
   s16x8 wb[SK_D][2][2];
   auto load_w = [&](int slot, int c) {
-    const int k = kbeg + min(c, nchunk - 1) * 64 + 8 * g;
+    const int kb = (kbeg + min(c, nchunk - 1) * 64) / PW_K;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) wb[slot][cb][ks] = *(const s16x8 *)(wr[cb] + k + 32 * ks);
+      for (int ks = 0; ks < 2; ++ks)
+        wb[slot][cb][ks] = *(const s16x8 *)(wr[cb] + (size_t)(kb + ks) * (PW_ROWS * PW_K));
   };
   // A stage prefetch: chunk e of the stage -> row e / (SK_KA/8), column 8 * (e % (SK_KA/8))
   s16x8 rah[ACH], ral[ACH];

@@ -53,6 +53,10 @@ struct GemmArgs {
   //   rows >= n_half (ffn_dim) are zero.
   const void *w[3];
   int seg_end[3];
+  // bf16 path: W packed (pack_weight) into 128-row panels of 32-wide k blocks; virtual row n,
+  // column k at ((n / 128) * (K / 32) + k / 32) * 4096 + (n % 128) * 32 + k % 32, rows past N
+  // zero up to the next multiple of 128.  w / seg_end are then unused.
+  const uint16_t *wp;
   int n_half;     // SwiGLU: ffn_dim
   int M, N, K;    // N is the virtual width (SwiGLU: 2 * ceil(ffn_dim / (BN/2)) * (BN/2))
   int k_split;    // K elements per split (multiple of the kernel's BK); gridDim.z splits
@@ -73,6 +77,16 @@ struct GemmArgs {
   // LMHEAD
   HeadPart *head_part; int n_vtiles; int vocab; int mask_id;
 };
+
+// Packed bf16 weights (the W layout of GemmArgs::wp).  PW_ROWS rows per panel, PW_K columns per
+// block.  Virtual rows: PACK_PLAIN: row n of src[0] (n < N); PACK_CONCAT: rows of src[0], then
+// src[1], then src[2], segment ends seg_end[0..2]; PACK_SWIGLU: panel t, row c < 64 -> gate row
+// 64 t + c of src[0], else up row 64 t + c - 64 of src[1], for rows < n_half.  Other rows are zero.
+static constexpr int PW_ROWS = 128, PW_K = 32;
+enum PackMode { PACK_PLAIN = 0, PACK_CONCAT = 1, PACK_SWIGLU = 2 };
+inline size_t packed_rows(int N) { return (size_t)(N + PW_ROWS - 1) / PW_ROWS * PW_ROWS; }
+hipError_t launch_pack_weight(uint16_t *dst, const void *const src[3], const int seg_end[3],
+                              int n_half, int mode, int N, int K, hipStream_t st);
 
 // Storage-type tag for templates: 0 = f32, 1 = bf16.
 // splits_out (may be NULL) receives the split-K count.  With EPI_RESID and more than one split

@@ -63,8 +63,9 @@ extern "C" {
  *   track table, backbones Dream and LLaDA): pre-norm RMSNorm, rotary positions
  *   (rotate-half form), attention with n_heads query heads over n_kv_heads K/V
  *   heads (n_heads % n_kv_heads == 0), SwiGLU feed-forward, untied embedding
- *   and lm_head, no biases.  Constraints: head_dim in {32, 64, 128}; for
- *   DLLM_BF16, d_model, n_heads*head_dim and ffn_dim are multiples of 64.
+ *   and lm_head, no biases.  Constraints: head_dim in {32, 64, 128};
+ *   d_model a multiple of 64 and at most 8192; for DLLM_BF16, n_heads*head_dim
+ *   and ffn_dim are multiples of 64.
  *   mask_id < vocab is the mask token; it is excluded from every softmax.
  *   logit_scale multiplies the lm_head output before the softmax.
  *   Knobs (Fast-dLLM README, Quick Start): gen_length is a multiple of
@@ -132,8 +133,13 @@ int dllm_workspace_bytes(const dllm_cfg *cfg, size_t *bytes);
  * Create a handle.  `workspace` is caller-owned device memory of ws_bytes
  * (>= dllm_workspace_bytes, 256-byte aligned); it holds the token state, the
  * KV cache (n_layers x batch x n_kv_heads x (prompt_len+gen_length) x head_dim
- * for K and V) and all intermediate buffers.  Initialises the workspace on
- * cfg.stream and synchronises it.
+ * for K and V, 4 bytes per element: fp32, or a bf16 hi and a bf16 lo plane),
+ * all intermediate buffers and, for DLLM_BF16, a packed copy of every linear
+ * weight (q/k/v, o, gate/up, down, lm_head): rows grouped into 128-row panels
+ * of 32-column blocks, so that a GEMM's weight tile is a few contiguous runs.
+ * dllm_create packs them; afterwards the linear weights are read only from the
+ * copy (embed and the norm gains are still read from the caller's pointers).
+ * Initialises the workspace on cfg.stream and synchronises it.
  */
 int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
                 dllm_t **out);

@@ -63,7 +63,15 @@ def test_workloads_validate_and_size(name):
     Lp = (L + 31) // 32 * 32
     # K and V: fp32, or bf16 hi + lo planes: 4 bytes per cached element either way
     kv = 2 * cfg["n_layers"] * cfg["batch"] * cfg["n_kv_heads"] * Lp * cfg["head_dim"] * 4
-    assert kv < n < kv + 40 * 2 ** 30
+    # bf16: a copy of every linear weight packed into 128-row panels (rows padded to 128)
+    wp = 0
+    if cfg["dtype"] == "bf16":
+        pad = lambda n: (n + 127) // 128 * 128  # noqa: E731
+        d, nq = cfg["d_model"], cfg["n_heads"] * cfg["head_dim"]
+        nkv, F = cfg["n_kv_heads"] * cfg["head_dim"], cfg["ffn_dim"]
+        per_layer = pad(nq + 2 * nkv) * d + pad(d) * nq + pad(2 * ((F + 63) // 64) * 64) * d + pad(d) * F
+        wp = 2 * (cfg["n_layers"] * per_layer + pad(cfg["vocab"]) * d)
+    assert kv + wp < n < kv + wp + 40 * 2 ** 30
 
 
 def test_long_context_workspace_fits_one_gpu():
