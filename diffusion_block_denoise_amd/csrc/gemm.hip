@@ -396,148 +396,6 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wide tiled bf16 MFMA kernel for many rows (block refresh).  128 x 256 tile, 4 waves as 2 x 2,
-// each wave 64 x 128 in 32x32 blocks (v_mfma_f32_32x32x16_bf16), BK = 32.
-//
-// Why this shape: per 16-wide K step a wave reads 2 A blocks (hi and lo) and 4 W blocks from
-// LDS for 16 MFMAs, 0.5 KB of LDS reads per MFMA instead of 0.75 KB for a 64 x 64 wave tile.
-// Tiles reach LDS by direct global->LDS loads (16 bytes per lane), so no staging registers and
-// no LDS write instructions; two stages alternate, and the loads of stage t+1 are issued right
-// after the fragments of stage t have been read, so they overlap stage t's MFMAs.
-//
-// LDS layout of a stage: A hi [128 rows][32 k], A lo [128][32], W [256][32], bf16.  A row is four
-// 16-byte chunks; chunk c of row r sits at position r*4 + (c ^ ((r >> 2) & 3)).  One load
-// instruction fills 64 consecutive positions, and a fragment read (16 lanes = 16 consecutive
-// rows, one chunk) hits 16 distinct 16-byte bank groups.
-static constexpr int WT_BM = 128, WT_BN = 256, WT_BK = 32;
-
-__device__ inline int wt_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__global__ __launch_bounds__(NT, 2) void gemm_wide_kernel(const GemmArgs a) {
-  constexpr int BM = WT_BM, BN = WT_BN, BK = WT_BK;
-  constexpr int A_BYTES = BM * BK * 2, W_BYTES = BN * BK * 2;
-  constexpr int STAGE = 2 * A_BYTES + W_BYTES;  // 32 KB
-  constexpr int LDC = 128 + 4;
-  constexpr int CT_BYTES = BM * LDC * 4;
-  constexpr int SMEM = 2 * STAGE > CT_BYTES ? 2 * STAGE : CT_BYTES;
-  __shared__ __align__(16) unsigned char smem[SMEM];
-  float *Ct = (float *)smem;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kbeg = blockIdx.z * a.k_split;
-  const int kend = min(a.K, kbeg + a.k_split);
-  const int T = (kend - kbeg) / BK;
-
-  // Per-lane sources of the direct loads.  A: instructions 2*wave + {0,1} of each plane, rows
-  // (slot >> 2); W: instructions 4*wave + {0..3}.  Rows past M read row M-1 and rows past N read
-  // row 0 of W: they only feed outputs that are never written.
-  size_t aoff[2];
-  int acol[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = (2 * wave + i) * 64 + lane, r = slot >> 2;
-    aoff[i] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda;
-    acol[i] = ((slot & 3) ^ ((r >> 2) & 3)) * 8;
-  }
-  // W: packed panels n0/128 and n0/128 + 1 (the second clamped to the last panel; its columns
-  // are then past N and never written)
-  const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
-  const uint16_t *wsrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = (4 * wave + i) * 64 + lane, r = slot >> 2;
-    wsrc[i] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K +
-              ((slot & 3) ^ ((r >> 2) & 3)) * 8;
-  }
-  auto issue = [&](int t, int buf) {
-    const int k0 = kbeg + t * BK;
-    unsigned char *st = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = 2 * wave + i;
-      __builtin_amdgcn_global_load_lds((const void *)((const uint16_t *)a.a_hi + aoff[i] + k0 + acol[i]),
-                                       (lds_void *)(st + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)((const uint16_t *)a.a_lo + aoff[i] + k0 + acol[i]),
-                                       (lds_void *)(st + A_BYTES + j * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * wave + i;
-      __builtin_amdgcn_global_load_lds((const void *)(wsrc[i] + (size_t)(k0 / PW_K) * (PW_ROWS * PW_K)),
-                                       (lds_void *)(st + 2 * A_BYTES + j * 1024), 16, 0, 0);
-    }
-  };
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int frow = lane & 31, fc = lane >> 5;
-  if (T > 0) issue(0, 0);
-  for (int t = 0; t < T; ++t) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage t have landed
-    __syncthreads();                      // ... and every wave's; stage t^1 is free again
-    const unsigned char *st = smem + (t & 1) * STAGE;
-    const uint16_t *Ah = (const uint16_t *)st, *Al = (const uint16_t *)(st + A_BYTES);
-    const uint16_t *Ws = (const uint16_t *)(st + 2 * A_BYTES);
-    bf16x8_t fa_hi[2][2], fa_lo[2][2], fb[2][4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int p = wt_pos(wm * 64 + i * 32 + frow, kk * 2 + fc) * 8;
-        fa_hi[kk][i] = *(const bf16x8_t *)(Ah + p);
-        fa_lo[kk][i] = *(const bf16x8_t *)(Al + p);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[kk][j] = *(const bf16x8_t *)(Ws + wt_pos(wn * 128 + j * 32 + frow, kk * 2 + fc) * 8);
-    }
-    if (t + 1 < T) issue(t + 1, (t + 1) & 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_hi[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_lo[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-        }
-  }
-  __syncthreads();
-  // Two 128-column halves through the C tile: the waves of half h write their accumulators, then
-  // the whole workgroup runs the epilogue of that 128 x 128 sub-tile.
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wn == h) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
-            Ct[row * LDC + j * 32 + (lane & 31)] = acc[i][j][r];
-          }
-    }
-    __syncthreads();
-    if (gridDim.z > 1)
-      write_partial<BM, 128>(a, Ct, LDC, m0, n0 + 128 * h);
-    else
-      run_epilogue<bf16, BM, 128>(a, Ct, LDC, m0, n0 + 128 * h);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 // Weight-streaming bf16 kernel for few rows (M <= 16*MT <= 64): the shape of a cached step, where
 // the time is the HBM read of W.  4 waves x 32 W rows = 128 columns per workgroup.
 //   W: each lane loads straight into the B-operand registers of v_mfma_f32_16x16x32_bf16 (lane:
