@@ -92,19 +92,43 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 
   const int kbeg = split * chunk;
   const int kend = min(rs.Lp, kbeg + chunk);
-  for (int kb = kbeg; kb < kend; kb += 32) {
+  // One 32-key tile's operands: K rows (hi/lo, 8 dims per k-step) and V^T runs (hi/lo, two runs
+  // of four keys per 16-key step).  A tile's K and V are loaded together, and the next tile's
+  // while the current one is computed, so the wave waits for one load latency per chunk rather
+  // than two per tile.
+  struct Tile {
+    bf16x8_t kh[KS], kl[KS];
+    bf16x4_t vh[DB][2][2], vl[DB][2][2];
+  };
+  auto load_tile = [&](int kb, Tile &t) {
+    const size_t krow = (size_t)(kb + col) * HD + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      t.kh[kk] = *(const bf16x8_t *)(Kh + krow + kk * 16);
+      t.kl[kk] = *(const bf16x8_t *)(Kl + krow + kk * 16);
+    }
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const size_t vrow = (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          t.vh[d][ks][r] = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8 * r);
+          t.vl[d][ks][r] = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8 * r);
+        }
+    }
+  };
+  auto compute_tile = [&](int kb, const Tile &t) {
     // S^T = K Q^T with hi/lo operands (the lo x lo term is below fp32 resolution).
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    const size_t krow = (size_t)(kb + col) * HD + half * 8;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8_t kh = *(const bf16x8_t *)(Kh + krow + kk * 16);
-      const bf16x8_t kl = *(const bf16x8_t *)(Kl + krow + kk * 16);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kk], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kk], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.kh[kk], qh[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.kl[kk], qh[kk], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.kh[kk], ql[kk], s, 0, 0, 0);
     }
     // s[i]: key kb + 8*(i/4) + 4*half + i%4, query col
     float tmax = -INFINITY;
@@ -135,23 +159,31 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-      const size_t vrow = (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x4_t h0 = *(const bf16x4_t *)(Vh + vrow + 16 * ks);
-        const bf16x4_t h1 = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8);
-        const bf16x4_t l0 = *(const bf16x4_t *)(Vl + vrow + 16 * ks);
-        const bf16x4_t l1 = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8);
         bf16x8_t vh, vl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vh[e] = h0[e]; vh[e + 4] = h1[e];
-          vl[e] = l0[e]; vl[e + 4] = l1[e];
+          vh[e] = t.vh[d][ks][0][e]; vh[e + 4] = t.vh[d][ks][1][e];
+          vl[e] = t.vl[d][ks][0][e]; vl[e + 4] = t.vl[d][ks][1][e];
         }
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[ks], o[d], 0, 0, 0);
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[ks], o[d], 0, 0, 0);
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl[ks], o[d], 0, 0, 0);
       }
+    }
+  };
+  // Unrolled by two so that the two tile buffers stay in fixed registers.  Past the chunk's end
+  // the prefetch re-reads the last tile (values unused), keeping the loads unconditional.
+  Tile ta, tb;
+  const int last = kend - 32;
+  if (kbeg < kend) load_tile(kbeg, ta);
+  for (int kb = kbeg; kb < kend; kb += 64) {
+    load_tile(min(kb + 32, last), tb);
+    compute_tile(kb, ta);
+    if (kb + 32 < kend) {
+      load_tile(min(kb + 64, last), ta);
+      compute_tile(kb + 32, tb);
     }
   }
   if (!valid) return;
