@@ -5,8 +5,9 @@
 // of G query heads shares every K/V load.  The wave computes S^T = K Q^T over 32 keys at a time:
 // in the MFMA output each lane holds one query and 16 keys, so the row softmax needs a single
 // cross-half shuffle.  The probabilities P^T are already laid out as the B operand of the next
-// MFMA, O^T += V^T P^T, whose A operand comes from the transposed V cache
-// ([hd][L] per head): every lane reads two runs of four consecutive keys.  No LDS is used.
+// MFMA, O^T += V^T P^T, whose A operand comes from the transposed V cache (bf16: per head,
+// 32-key tiles of [hd][32], so a tile is one contiguous run): every lane reads two runs of four
+// consecutive keys.  No LDS is used.
 // q, K, V^T and P are bf16 hi/lo pairs (hi + lo carries about 16 mantissa bits): every product
 // is hi*hi + lo*hi + hi*lo in fp32 accumulators.  A single bf16 rounding of K, V, q or P moves
 // the 32-layer, d=4096 model's confidences by several percent; the pairs keep the attention at
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
       for (int e = 0; e < 8; ++e) qh[kk][e] = ql[kk][e] = (__bf16)0.f;
     }
   }
-  const size_t kv_off = (size_t)bg * rs.Lp * HD;  // same for K [Lp][HD] and V^T [HD][Lp]
+  // K [Lp][HD]; V^T in 32-key tiles [Lp/32][HD][32]; both HD * Lp per (batch row, K/V head)
+  const size_t kv_off = (size_t)bg * rs.Lp * HD;
   const bf16 *Kh = k_hi + kv_off, *Kl = k_lo + kv_off;
   const bf16 *Vh = vt_hi + kv_off, *Vl = vt_lo + kv_off;
 
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     }
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const size_t vrow = (size_t)(d * 32 + col) * rs.Lp + kb + 4 * half;
+      const size_t vrow = (size_t)(kb >> 5) * (HD * 32) + (d * 32 + col) * 32 + 4 * half;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
                             (const uint16_t *)vt_hi + kv_off, (const uint16_t *)vt_lo + kv_off};
 
   // chunk c of a stage: plane = c / (32*HD/8); K planes: key c' / (HD/8), dims 8*(c' % (HD/8));
-  // V^T planes: dim c' / 4, keys 8*(c' % 4)
+  // V^T planes (a contiguous [HD][32] tile): dim c' / 4, keys 8*(c' % 4)
   s16x8 pre[CPT];
   auto load_tile = [&](int kb) {
 #pragma unroll
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
       const int c = tid + i * NTH, plane = c / (32 * HD / 8), cc = c % (32 * HD / 8);
       size_t off;
       if (plane < 2) off = (size_t)(kb + cc / (HD / 8)) * HD + 8 * (cc % (HD / 8));
-      else off = (size_t)(cc / 4) * rs.Lp + kb + 8 * (cc % 4);
+      else off = (size_t)(kb >> 5) * (HD * 32) + 8 * cc;  // V^T tile: contiguous
       pre[i] = *(const s16x8 *)(src[plane] + off);
     }
   };
