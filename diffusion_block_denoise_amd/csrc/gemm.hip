@@ -591,15 +591,18 @@ static void split_plan(int M, int N, int K, int dtype, int &splits, int &kc) {
     want = (int)(cap / tiles);
     max_splits = std::min(K / 512, 8);
   } else {
-    // Rounds of resident workgroups (2 per CU) times K steps per split, plus 6% per extra split
-    // for the partial traffic and the reduce; at most 16 splits of at least 4 K steps.
+    // Estimated time (us): rounds of resident workgroups (2 per CU) times the K steps of a
+    // split at ~1.8 us per step and round, plus the round trip of the fp32 partial tiles
+    // (written here, read by the reduce) at ~5 TB/s when split.  At most 16 splits of at
+    // least 4 K steps.  (Fitted to the 768-row projections of the 8B shape on MI355X.)
     const int iters = K / 64;
     const long slots = 512;
     double best = 1e30;
     want = 1;
     for (int sp = 1; sp <= 16 && sp <= std::max(1, iters / 4); ++sp) {
       const long rounds = (tiles * sp + slots - 1) / slots;
-      const double cost = (double)rounds * ((iters + sp - 1) / sp) * (1.0 + 0.06 * (sp - 1));
+      const double partial_us = sp > 1 ? sp * (double)M * N * 8.0 / 5.0e6 : 0.0;
+      const double cost = 1.8 * rounds * ((iters + sp - 1) / sp) + partial_us;
       if (cost < best - 1e-9) { best = cost; want = sp; }
     }
     max_splits = std::max(1, K / 256);
