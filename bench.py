@@ -65,6 +65,29 @@ def phase_latency(h, prompt, cfg):
     return med(refresh), med(step)
 
 
+def counter_traffic(kernel_class):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when there is none or the kernel's source has changed since the
+    counters were taken (its sha256 no longer matches)."""
+    import glob
+    import hashlib
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+        if not m:
+            continue
+        d = json.loads(m.group(1))
+        if d.get("kernel_class") != kernel_class:
+            continue
+        src = os.path.join(ROOT, d["source"])
+        if not os.path.exists(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != d["source_sha256"]:
+            return None
+        return d["traffic_bytes_per_dispatch"]
+    return None
+
+
 def roofline(prof, dtype):
     """Roofline entry for the kernel class with the largest timed share."""
     name, k = max(prof.items(), key=lambda kv: kv[1]["ms"])
@@ -75,11 +98,11 @@ def roofline(prof, dtype):
         peak = BF16_PEAK_TFLOPS if dtype == "bf16" else F32_PEAK_TFLOPS
         ach = k["flops"] / t / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                "frac": ach / peak, "traffic": None, "kernel": name,
+                "frac": ach / peak, "traffic": counter_traffic(name), "kernel": name,
                 "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
     ach = k["bytes"] / t / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": name,
+            "frac": ach / HBM_PEAK_GBS, "traffic": counter_traffic(name), "kernel": name,
             "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
 
 
