@@ -27,6 +27,14 @@ What it follows
   cache), and attend to the cached K/V of the others.  With no cache every
   step is a full forward (Streaming-dLLM README tables: "Prefix-Cache" and
   "Fast-dLLM" columns against the no-cache backbone).
+* Approximate suffix pruning (Streaming-dLLM README, figure caption on
+  approximated suffix pruning; ES-dLLM paper card, Streaming-dLLM abstract:
+  pruning redundant mask tokens of the suffix).  While block [s, e) is decoded
+  the model sees only the prefix, the block, the window of the ``suffix_window``
+  positions right after the block and the trailing position L-1; every other
+  suffix position is absent, for the block's refresh as well as its steps.  The
+  kept positions keep their own rotary positions.  ``suffix_window < 0`` keeps
+  the whole context.
 """
 
 from __future__ import annotations
@@ -114,23 +122,34 @@ class Decoder:
         s = self.P + b * self.Bs
         return s, s + self.Bs
 
+    def active(self, b: int) -> np.ndarray:
+        """Positions the model sees while block b is decoded: all of them, or with suffix
+        pruning [0, e + W) and the trailing position L-1."""
+        _, e = self.block_range(b)
+        W = self.cfg.get("suffix_window", -1)
+        if W < 0 or e + W >= self.L - 1:
+            return np.arange(self.L)
+        return np.concatenate([np.arange(e + W), [self.L - 1]])
+
     # -- forwards ------------------------------------------------------------------------
     def _full(self) -> list:
         s, e = self.block_range(self.block)
+        act = self.active(self.block)
         out = []
         for r in range(self.B):
-            h = self.m.forward(self.x[r], 0, self.L, self.caches[r])
-            out.append(self.m.stats(h[s:e]))
+            h = self.m.forward_rows(self.x[r], act, act, self.caches[r])
+            out.append(self.m.stats(h[s:e]))  # act[i] == i for every i < e
         self.forwards["full"] += 1
         return out
 
     def _cached(self) -> list:
         s, e = self.block_range(self.block)
+        act = self.active(self.block)
         mode = self.cfg["use_cache"]
-        stop = e if mode == DUAL_CACHE else self.L
+        rows = np.arange(s, e) if mode == DUAL_CACHE else act[act >= s]
         out = []
         for r in range(self.B):
-            h = self.m.forward(self.x[r], s, stop, self.caches[r])
+            h = self.m.forward_rows(self.x[r], rows, act, self.caches[r])
             out.append(self.m.stats(h[:self.Bs]))
         self.forwards["cached"] += 1
         return out

@@ -138,19 +138,34 @@ class Model:
                 [np.zeros(shp) for _ in range(self.cfg["n_layers"])])
 
     def forward(self, x: np.ndarray, start: int, stop: int, cache) -> np.ndarray:
-        """Forward of rows [start, stop) of one sequence x [L].
+        """Forward of rows [start, stop) of one sequence x [L], attending to all L positions.
 
         Rows outside [start, stop) contribute their cached K/V only.  K/V of the
         rows in the range are written to ``cache`` first, so the queries see the
         fresh values for their own rows.  Returns the final hidden states
         (before the final norm) of the rows, [stop - start, d].
         """
+        return self.forward_rows(x, np.arange(start, stop), np.arange(self.L), cache)
+
+    def forward_rows(self, x: np.ndarray, rows, keys, cache) -> np.ndarray:
+        """Forward of the row positions ``rows`` of one sequence x [L], whose queries attend
+        to the positions ``keys`` only (``rows`` must be among them).
+
+        Every position keeps its own index as its rotary position.  With
+        ``keys = range(L)`` this is the full-context forward; a shorter ``keys``
+        is the pruned context of approximate suffix pruning (the positions not in
+        ``keys`` are absent for the model).  K/V of the rows are written to the
+        cache at their positions first.  Returns the final hidden states of the
+        rows, [len(rows), d].
+        """
         cfg = self.cfg
         eps = cfg["rms_eps"]
         ck, cv = cache
-        n = stop - start
-        h = self._W("embed")[x[start:stop]]
-        cos, sin = rope_tables(np.arange(start, stop), self.hd, cfg["rope_base"])
+        rows = np.asarray(rows, dtype=np.int64)
+        keys = np.asarray(keys, dtype=np.int64)
+        n = len(rows)
+        h = self._W("embed")[x[rows]]
+        cos, sin = rope_tables(rows, self.hd, cfg["rope_base"])
         for l in range(cfg["n_layers"]):
             p = f"layers.{l}."
             a = rms_norm(h, self._W(p + "attn_norm"), eps)
@@ -159,9 +174,9 @@ class Model:
             v = (a @ self._W(p + "wv").T).reshape(n, self.Hkv, self.hd)
             q = apply_rope(q, cos, sin)
             k = apply_rope(k, cos, sin)
-            ck[l][start:stop] = k
-            cv[l][start:stop] = v
-            o = attention(q, ck[l], cv[l]).reshape(n, self.H * self.hd)
+            ck[l][rows] = k
+            cv[l][rows] = v
+            o = attention(q, ck[l][keys], cv[l][keys]).reshape(n, self.H * self.hd)
             h = h + o @ self._W(p + "wo").T
             f = rms_norm(h, self._W(p + "ffn_norm"), eps)
             h = h + swiglu_ffn(f, self._W(p + "w_gate"), self._W(p + "w_up"),

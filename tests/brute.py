@@ -41,10 +41,14 @@ class Brute:
         self.K = [[[None] * Hkv for _ in range(self.L)] for _ in range(nl)]
         self.V = [[[None] * Hkv for _ in range(self.L)] for _ in range(nl)]
 
-    def forward_rows(self, x, rows):
+    def forward_rows(self, x, rows, pos=None):
+        """Forward of indices ``rows`` of the token list x; index i sits at rotary position
+        pos[i] (default i).  Every query attends to all len(x) indices."""
         cfg = self.cfg
         H, Hkv, hd, eps = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["rms_eps"]
         W = self.W
+        n = len(x)
+        pos = list(range(n)) if pos is None else pos
         hs = {p: list(W["embed"][x[p]]) for p in rows}
         for l in range(cfg["n_layers"]):
             pre = f"layers.{l}."
@@ -54,20 +58,20 @@ class Brute:
                 q = _matvec(W[pre + "wq"], a)
                 k = _matvec(W[pre + "wk"], a)
                 v = _matvec(W[pre + "wv"], a)
-                qs[p] = [_rope(q[j * hd:(j + 1) * hd], p, cfg["rope_base"]) for j in range(H)]
+                qs[p] = [_rope(q[j * hd:(j + 1) * hd], pos[p], cfg["rope_base"]) for j in range(H)]
                 for g in range(Hkv):
-                    self.K[l][p][g] = _rope(k[g * hd:(g + 1) * hd], p, cfg["rope_base"])
+                    self.K[l][p][g] = _rope(k[g * hd:(g + 1) * hd], pos[p], cfg["rope_base"])
                     self.V[l][p][g] = v[g * hd:(g + 1) * hd]
             for p in rows:
                 o = []
                 for j in range(H):
                     g = j * Hkv // H
                     sc = [sum(qs[p][j][t] * self.K[l][m][g][t] for t in range(hd)) / math.sqrt(hd)
-                          for m in range(self.L)]
+                          for m in range(n)]
                     mx = max(sc)
                     e = [math.exp(v - mx) for v in sc]
                     tot = sum(e)
-                    o += [sum(e[m] / tot * self.V[l][m][g][t] for m in range(self.L)) for t in range(hd)]
+                    o += [sum(e[m] / tot * self.V[l][m][g][t] for m in range(n)) for t in range(hd)]
                 hs[p] = [a + b for a, b in zip(hs[p], _matvec(W[pre + "wo"], o))]
                 f = _rms(hs[p], W[pre + "ffn_norm"], eps)
                 gt = _matvec(W[pre + "w_gate"], f)
@@ -96,17 +100,25 @@ class Brute:
         spb = (cfg["steps"] or G) // nb
         x = list(prompt) + [mask] * G
         steps = []
+        win = cfg.get("suffix_window", -1)
         for b in range(nb):
             s, e = P + b * Bs, P + (b + 1) * Bs
+            # suffix pruning: the model runs on the shorter sequence of the kept positions
+            # (prefix, block, the window after the block, the last position), each keeping its
+            # rotary position; its cache is indexed by the short sequence
+            if win < 0 or e + win >= self.L - 1:
+                keep = list(range(self.L))
+            else:
+                keep = list(range(e + win)) + [self.L - 1]
             j = 0
             while any(x[i] == mask for i in range(s, e)):
                 if j == 0 or refresh_every_step or cfg["use_cache"] == 0:
-                    rows = list(range(self.L))
+                    rows = list(range(len(keep)))
                 elif cfg["use_cache"] == 1:
-                    rows = list(range(s, self.L))
+                    rows = list(range(s, len(keep)))
                 else:
                     rows = list(range(s, e))
-                hs = self.forward_rows(x, rows)
+                hs = self.forward_rows([x[p] for p in keep], rows, keep)
                 st = {p: self.stats(hs[p]) for p in range(s, e)}
                 k = max(1, Bs // spb + (1 if j < Bs % spb else 0))
                 masked = [p for p in range(s, e) if x[p] == mask]
