@@ -35,13 +35,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def phase_latency(h, prompt, cfg):
-    """Median block-refresh and cached-step latency (ms), timed with events on the stream."""
+def phase_latency(h, prompt, cfg, nb):
+    """Median block-refresh and cached-step latency (ms) over the first nb blocks, timed with
+    events on the stream."""
     import torch
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     h.prefill(prompt)
     refresh, step = [], []
-    nb = cfg["gen_length"] // cfg["block_size"]
     for b in range(nb):
         if b:
             e0, e1 = ev(), ev()
@@ -106,13 +106,14 @@ def roofline(prof, dtype):
             "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
 
 
-def cpu_baseline(cfg, W, n_full, n_cached, sample_layers=2):
+def cpu_baseline(cfg, W, n_full, n_cached, tokens, sample_layers=2):
     """The oracle on a bounded sample: `sample_layers` of the model's layers, one refresh forward
-    over all positions and one dual-cache step over the block rows of batch row 0, plus the
+    over block 1's context and one dual-cache step over its block rows in batch row 0, plus the
     lm_head statistics; scaled by n_layers / sample_layers and projected with the GPU run's
     refresh and cached-step counts."""
     import numpy as np
     import synth
+    from oracle import decode as od
     from oracle import model as om
     nl = cfg["n_layers"]
     sc = dict(cfg, n_layers=sample_layers)
@@ -120,24 +121,24 @@ def cpu_baseline(cfg, W, n_full, n_cached, sample_layers=2):
     w_host = {n: W[n].float().cpu().numpy() for n in names}
     m = om.Model(sc, w_host)
     x = synth.block_state_np(cfg, 1)[0].astype(np.int64)
-    L = len(x)
+    act = od.Decoder(m).active(1)  # block 1's context (all positions unless pruned)
+    L = len(act)
     s = cfg["prompt_len"] + cfg["block_size"]
     e = s + cfg["block_size"]
     cache = m.new_cache()
     t0 = time.perf_counter()
-    hid = m.forward(x, 0, L, cache)
+    hid = m.forward_rows(x, act, act, cache)
     t_full = time.perf_counter() - t0
     t0 = time.perf_counter()
     m.stats(hid[s:e])
     t_stats = time.perf_counter() - t0
     t0 = time.perf_counter()
-    hid = m.forward(x, s, e, cache)
+    hid = m.forward_rows(x, np.arange(s, e), act, cache)
     t_step = time.perf_counter() - t0
     scale = nl / sample_layers
     T_refresh = t_full * scale + t_stats
     T_step = t_step * scale + t_stats
     total = cfg["batch"] * (n_full * T_refresh + n_cached * T_step)
-    tokens = cfg["batch"] * cfg["gen_length"]
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": tokens / total, "unit": "tokens/s (projected)", "cores": min(cores, threads),
@@ -159,6 +160,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip the event-instrumented pass (roofline and kernel classes)")
+    ap.add_argument("--suffix-window", type=int, default=None,
+                    help="approximate suffix pruning window (default: the workload's, -1 = off)")
+    ap.add_argument("--blocks", type=int, default=0,
+                    help="time prefill plus only the first N blocks (default: the whole generate)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -185,6 +190,10 @@ def main():
     from diffusion_block_denoise_amd import dllm
 
     cfg = synth.configs.get(args.workload)
+    if args.suffix_window is not None:
+        cfg["suffix_window"] = args.suffix_window
+    nb_all = cfg["gen_length"] // cfg["block_size"]
+    nblocks = args.blocks if 0 < args.blocks < nb_all else nb_all
     torch.cuda.set_device(0)
     t0 = time.time()
     W = synth.weights_torch(cfg, device="cuda")
@@ -192,21 +201,36 @@ def main():
     log(f"weights generated in {time.time() - t0:.1f}s")
     h = dllm.Handle(cfg, W)
     prompt = synth.prompt_np(cfg)
+
+    def run():
+        """One step: the whole generate, or prefill plus the first `nblocks` blocks."""
+        if nblocks == nb_all:
+            return h.generate(prompt)[1]
+        h.prefill(prompt)
+        for b in range(nblocks):
+            if b:
+                h.block_begin(b)
+            done = False
+            while not done:
+                _, done = h.denoise_step()
+        return h.get_stats()
+
     for i in range(args.warmup):
-        _, st = h.generate(prompt)
+        st = run()
         log(f"warmup {i}: {st['steps']} denoise steps")
-    # Timed region: plain generates, no instrumentation.
+    # Timed region: plain decode calls, no instrumentation.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     stats = []
     for i in range(args.steps):
-        _, st = h.generate(prompt)
+        st = run()
         stats.append(st)
         log(f"step {i}: {st['steps']} denoise steps")
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     B, G = cfg["batch"], cfg["gen_length"]
-    value = B * G * args.steps / el
+    tokens = B * cfg["block_size"] * nblocks
+    value = tokens * args.steps / el
     # Kernel-class durations: the same generate again with HIP events around every launch of the
     # three classes, on the handle's stream (events add a gap per launch, so this pass is not the
     # timed one).
@@ -215,14 +239,16 @@ def main():
         mask = (1 << dllm.DLLM_KC_GEMM_SKINNY) | (1 << dllm.DLLM_KC_GEMM_TILED) | \
             (1 << dllm.DLLM_KC_ATTENTION)
         h.set_profiling(mask)
-        h.generate(prompt)
+        run()
         prof = h.get_profile()
         h.set_profiling(0)
         roof, dom = roofline(prof, cfg["dtype"])
-    refresh_ms, step_ms = phase_latency(h, prompt, cfg)
+    refresh_ms, step_ms = phase_latency(h, prompt, cfg, nblocks)
     st = stats[-1]
     out = {
-        "metric": "committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)",
+        "metric": ("committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)"
+                   if cfg["name"] == "llada8b" and cfg["suffix_window"] < 0 and nblocks == nb_all
+                   else f"committed tokens/s ({cfg['name']})"),
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
@@ -230,7 +256,8 @@ def main():
         "config": {"workload": cfg["name"], "layers": cfg["n_layers"], "d_model": cfg["d_model"],
                    "batch": B, "prompt_len": cfg["prompt_len"], "gen_length": G,
                    "block_size": cfg["block_size"], "threshold": cfg["threshold"],
-                   "use_cache": ["none", "prefix", "dual"][cfg["use_cache"]]},
+                   "use_cache": ["none", "prefix", "dual"][cfg["use_cache"]],
+                   "suffix_window": cfg["suffix_window"], "blocks_timed": nblocks},
         "roofline": roof,
         "denoise_steps_per_generate": st["steps"],
         "refreshes_per_generate": st["full_forwards"],
@@ -244,7 +271,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         t0 = time.time()
-        out["cpu_baseline"] = cpu_baseline(cfg, W, st["full_forwards"], st["cached_forwards"])
+        out["cpu_baseline"] = cpu_baseline(cfg, W, st["full_forwards"], st["cached_forwards"],
+                                           tokens)
         log(f"cpu baseline sample took {time.time() - t0:.1f}s")
     print(json.dumps(out), flush=True)
 

@@ -31,12 +31,12 @@ static inline int attn_tiles(RowSet rs, int H, int Hkv) {
 
 static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk) {
   const long waves = (long)attn_tiles(rs, H, Hkv) * rs.B * Hkv;
-  const int kt = rs.Lp / 32;  // 32-key tiles
+  const int kt = (rs.L + 31) / 32;  // 32-key tiles of the context
   int want = (int)((256 + waves - 1) / waves);
   if (want > kt) want = kt;
   if (want < 1) want = 1;
   chunk = (kt + want - 1) / want * 32;
-  splits = (rs.Lp + chunk - 1) / chunk;
+  splits = (kt * 32 + chunk - 1) / chunk;
 }
 
 size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
 
   const int kbeg = split * chunk;
-  const int kend = min(rs.Lp, kbeg + chunk);
+  const int kend = min((rs.L + 31) / 32 * 32, kbeg + chunk);
   // One 32-key tile's operands: K rows (hi/lo, 8 dims per k-step) and V^T runs (hi/lo, two runs
   // of four keys per 16-key step).  A tile's K and V are loaded together, and the next tile's
   // while the current one is computed, so the wave waits for one load latency per chunk rather
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
 
-  const int ntile = rs.Lp / 32;
+  const int ntile = (rs.L + 31) / 32;
   load_tile(0);
   store_tile(lds);
   load_tile(min(1, ntile - 1) * 32);

@@ -86,6 +86,7 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
 // Workspace plan
 struct Plan {
   int B, P, G, Bs, L, Lp, NB, spb, d, H, Hkv, hd, F, V, nq, nkv, dt;
+  int W;  // suffix window (< 0: whole context)
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
@@ -97,9 +98,30 @@ struct Plan {
   int n_vtiles;
 };
 
+// Rows [start, start + nR) of every batch row, over the full context.
 RowSet rows_of(const Plan &p, int start, int nR) {
   RowSet r;
   r.B = p.B; r.L = p.L; r.Lp = p.Lp; r.start = start; r.nR = nR;
+  r.Lx = p.L; r.tail = -1;
+  return r;
+}
+
+// Context of block b (approximate suffix pruning, Streaming-dLLM): the prefix, the block, the
+// W positions after it and the last position, compacted to slots [0, e + W] with the last
+// position in slot e + W; the whole sequence when W < 0 or the window reaches the end.
+int context_len(const Plan &p, int b, int *tail) {
+  const int e = p.P + (b + 1) * p.Bs;
+  if (p.W < 0 || e + p.W >= p.L - 1) {
+    *tail = -1;
+    return p.L;
+  }
+  *tail = e + p.W;
+  return e + p.W + 1;
+}
+
+RowSet rows_in_context(const Plan &p, int b, int start, int nR) {
+  RowSet r = rows_of(p, start, nR);
+  r.L = context_len(p, b, &r.tail);
   return r;
 }
 
@@ -111,14 +133,21 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.d = c->d_model; p.H = c->n_heads; p.Hkv = c->n_kv_heads; p.hd = c->head_dim;
   p.F = c->ffn_dim; p.V = c->vocab; p.nq = p.H * p.hd; p.nkv = p.Hkv * p.hd;
   p.dt = c->dtype == DLLM_BF16 ? 1 : 0;
+  p.W = c->suffix_window;
   const size_t Mmax = (size_t)p.B * p.L;
   p.Mmax = Mmax;
   p.kv_layer_elems = (size_t)p.B * p.Hkv * p.Lp * p.hd;
 
-  // Row counts that a forward can have: refresh / no cache (B*L), dual step (B*Bs), prefix
-  // step of block b (B*(L - s_b)).
+  // Row counts that a forward can have: refresh / no cache (B*L, or B*Lc_b with suffix
+  // pruning), dual step (B*Bs), prefix step of block b (B*(L - s_b) or B*(Lc_b - s_b)).
   std::vector<int> Ms = {p.B * p.L, p.B * p.Bs};
-  for (int b = 0; b < p.NB; ++b) Ms.push_back(p.B * (p.L - (p.P + b * p.Bs)));
+  for (int b = 0; b < p.NB; ++b) {
+    int tail;
+    const int Lc = context_len(p, b, &tail), s0 = p.P + b * p.Bs;
+    Ms.push_back(p.B * (p.L - s0));
+    Ms.push_back(p.B * Lc);
+    Ms.push_back(p.B * (Lc - s0));
+  }
   size_t gpart = 0, apart = 0;
   for (int M : Ms) {
     const int bn = gemm_bn(M, p.dt);
@@ -471,7 +500,9 @@ int head(dllm_t *h) {
 }
 
 int refresh(dllm_t *h) {
-  int rc = forward(h, rows_of(h->p, 0, h->p.L));
+  int tail;
+  const int Lc = context_len(h->p, h->block, &tail);
+  int rc = forward(h, rows_in_context(h->p, h->block, 0, Lc));
   if (rc) return rc;
   h->stats.full_forwards++;
   return head(h);
@@ -519,8 +550,10 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
     if (h->cfg.use_cache == DLLM_NO_CACHE || h->cfg.refresh_every_step) {
       rc = refresh(h);
     } else {
-      const int stop = h->cfg.use_cache == DLLM_DUAL_CACHE ? s + p.Bs : p.L;
-      rc = forward(h, rows_of(p, s, stop - s));
+      int tail;
+      const int Lc = context_len(p, h->block, &tail);
+      const int stop = h->cfg.use_cache == DLLM_DUAL_CACHE ? s + p.Bs : Lc;
+      rc = forward(h, rows_in_context(p, h->block, s, stop - s));
       if (!rc) {
         h->stats.cached_forwards++;
         rc = head(h);

@@ -157,7 +157,8 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
         const float x = Ct[r * ldc + c];
         if (n < nq + nk) {
           const int j = i < half ? i : i - half;
-          const float cs = a.rope_cos[(size_t)p * half + j], sn = a.rope_sin[(size_t)p * half + j];
+          const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angle of the slot's position
+        const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
           const float y = i < half ? x * cs - Ct[r * ldc + c + half] * sn
                                    : x * cs + Ct[r * ldc + c - half] * sn;
           if (n < nq) {

@@ -12,13 +12,20 @@ typedef __hip_bfloat16 bf16;
 
 // Rows that one forward processes: for each batch row b, positions [start, start + nR).
 // Row m of every activation buffer is (b = m / nR, position = start + m % nR).
+// Rows of a forward.  Positions are cache-slot indices c in [0, L): the model's context.
+// With suffix pruning the context is the compacted sequence [0, L - 1) plus one slot, the
+// `tail`, that carries the last position Lx - 1 of the token state; pos(c) is the position
+// (token index and rotary angle) of slot c.  Without pruning tail = -1 and pos(c) = c.
 struct RowSet {
   int B;      // batch rows
-  int L;      // sequence length (positions per batch row)
-  int Lp;     // cache slots per batch row and head: L rounded up to a multiple of 32
-  int start;  // first position
-  int nR;     // positions per batch row
-  int M() const { return B * nR; }
+  int L;      // context length: keys every query attends to (slots [0, L))
+  int Lp;     // cache slots per batch row and head: the full length rounded up to 32
+  int start;  // first slot of the rows
+  int nR;     // rows per batch row
+  int Lx;     // token-state length per batch row (prompt + generation)
+  int tail;   // slot that holds position Lx - 1, or -1
+  __host__ __device__ int M() const { return B * nR; }
+  __host__ __device__ int pos(int c) const { return c == tail ? Lx - 1 : c; }
 };
 
 // GEMM epilogues.  The GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (fp32 accumulate).

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(RN_NT) void embed_norm_kernel(const int *x, const T
                                                            bf16 *a_lo, float *a_f32) {
   const int m = blockIdx.x;
   const int b = m / rs.nR, p = rs.start + m % rs.nR;
-  const int tok = x[(size_t)b * rs.L + p];
+  const int tok = x[(size_t)b * rs.Lx + rs.pos(p)];
   const T *er = embed + (size_t)tok * d;
   float4 v[RN_MAX_C];
   float ss = 0.f;

@@ -76,6 +76,11 @@ extern "C" {
  *   softmax probability) is strictly greater; use_cache: DLLM_*_CACHE.
  *   block_size <= 256.  refresh_every_step != 0 refreshes the whole cache at
  *   every step (a test hook: it must reproduce no-cache decoding).
+ *   suffix_window >= 0 turns on approximate suffix pruning (Streaming-dLLM
+ *   README, figure caption on approximated suffix pruning): while block [s, e)
+ *   is decoded the model sees only positions [0, e + suffix_window) and the
+ *   last position, each at its own rotary position, for the block's refresh
+ *   and its steps; the other suffix positions are absent.  < 0: whole context.
  *   All batch rows share prompt_len and advance block by block together.
  */
 typedef struct dllm_cfg {
@@ -87,6 +92,7 @@ typedef struct dllm_cfg {
   float threshold;
   int32_t use_cache;
   int32_t refresh_every_step;
+  int32_t suffix_window;
   void *stream; /* hipStream_t */
 } dllm_cfg;
 

@@ -39,7 +39,8 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu %zu\\n", sizeof(dllm_cfg), offsetof(dllm_cfg, threshold),
          offsetof(dllm_cfg, stream), sizeof(dllm_weights), sizeof(dllm_stats));
-  printf("%zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step));
+  printf("%zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
+         offsetof(dllm_cfg, suffix_window));
   return 0;
 }}
 """)
@@ -49,7 +50,8 @@ int main(void) {{
     got = [int(v) for v in out]
     want = [C.sizeof(dllm.dllm_cfg), dllm.dllm_cfg.threshold.offset, dllm.dllm_cfg.stream.offset,
             C.sizeof(dllm.dllm_weights), C.sizeof(dllm.dllm_stats),
-            dllm.dllm_stats.commits_hist.offset, dllm.dllm_stats.ms_step.offset]
+            dllm.dllm_stats.commits_hist.offset, dllm.dllm_stats.ms_step.offset,
+            dllm.dllm_cfg.suffix_window.offset]
     assert got == want
 
 
