@@ -35,6 +35,15 @@ What it follows
   suffix position is absent, for the block's refresh as well as its steps.  The
   kept positions keep their own rotary positions.  ``suffix_window < 0`` keeps
   the whole context.
+* Block-causal attention (``attention == "block_causal"``; Fast-dLLM README
+  track table, v2 "Block Diffusion"; Streaming-dLLM README, the note on
+  block-causal diffusion models and the Open Pangu table).  The prompt is one
+  block and the generation is split into blocks of ``block_size``; a query sees
+  every key of its own block and of the blocks before it, nothing after.  A
+  finished block's K/V therefore never change: the refresh at block b computes
+  only block b-1 (its tokens are now final; for b = 0 the prompt) and block b,
+  and every later step recomputes block b.  Suffix pruning does not apply
+  (nothing after the block is visible).
 """
 
 from __future__ import annotations
@@ -122,6 +131,18 @@ class Decoder:
         s = self.P + b * self.Bs
         return s, s + self.Bs
 
+    def block_causal(self) -> bool:
+        return self.cfg.get("attention", "full") == "block_causal"
+
+    def block_end(self, p: int) -> int:
+        """End of the block that position p belongs to (the prompt is one block)."""
+        if p < self.P:
+            return self.P
+        return self.P + ((p - self.P) // self.Bs + 1) * self.Bs
+
+    def _limits(self, rows) -> np.ndarray:
+        return np.array([self.block_end(int(p)) for p in rows])
+
     def active(self, b: int) -> np.ndarray:
         """Positions the model sees while block b is decoded: all of them, or with suffix
         pruning [0, e + W) and the trailing position L-1."""
@@ -134,6 +155,16 @@ class Decoder:
     # -- forwards ------------------------------------------------------------------------
     def _full(self) -> list:
         s, e = self.block_range(self.block)
+        if self.block_causal():
+            # block b-1 (now final; for b = 0 the prompt) and block b, each with its own keys
+            rows = np.arange(s - self.Bs if self.block > 0 else 0, e)
+            out = []
+            for r in range(self.B):
+                h = self.m.forward_rows(self.x[r], rows, np.arange(e), self.caches[r],
+                                        self._limits(rows))
+                out.append(self.m.stats(h[s - rows[0]:]))
+            self.forwards["full"] += 1
+            return out
         act = self.active(self.block)
         out = []
         for r in range(self.B):
@@ -144,6 +175,15 @@ class Decoder:
 
     def _cached(self) -> list:
         s, e = self.block_range(self.block)
+        if self.block_causal():
+            rows = np.arange(s, e)
+            out = []
+            for r in range(self.B):
+                h = self.m.forward_rows(self.x[r], rows, np.arange(e), self.caches[r],
+                                        self._limits(rows))
+                out.append(self.m.stats(h))
+            self.forwards["cached"] += 1
+            return out
         act = self.active(self.block)
         mode = self.cfg["use_cache"]
         rows = np.arange(s, e) if mode == DUAL_CACHE else act[act >= s]

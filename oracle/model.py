@@ -31,8 +31,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["rms_norm", "rope_tables", "apply_rope", "attention", "silu", "swiglu_ffn",
-           "head_stats", "Model"]
+__all__ = ["rms_norm", "rope_tables", "apply_rope", "attention", "attention_limited", "silu",
+           "swiglu_ffn", "head_stats", "Model"]
 
 
 def rms_norm(h: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -79,6 +79,26 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         out[:, j, :] = p @ v[:, g, :]
+    return out
+
+
+def attention_limited(q: np.ndarray, k: np.ndarray, v: np.ndarray, key_pos, limits) -> np.ndarray:
+    """attention() where query i sees only the keys whose position is below limits[i].
+
+    q [nq, H, hd]; k, v [nk, Hkv, hd] at positions key_pos [nk]; limits [nq].
+    """
+    nq, H, hd = q.shape
+    Hkv = k.shape[1]
+    group = H // Hkv
+    key_pos = np.asarray(key_pos)
+    out = np.empty_like(q)
+    for i in range(nq):
+        sel = key_pos < limits[i]
+        for j in range(H):
+            g = j // group
+            s = q[i, j, :] @ k[sel, g, :].T / np.sqrt(hd)
+            p = np.exp(s - s.max())
+            out[i, j, :] = (p / p.sum()) @ v[sel, g, :]
     return out
 
 
@@ -147,16 +167,17 @@ class Model:
         """
         return self.forward_rows(x, np.arange(start, stop), np.arange(self.L), cache)
 
-    def forward_rows(self, x: np.ndarray, rows, keys, cache) -> np.ndarray:
+    def forward_rows(self, x: np.ndarray, rows, keys, cache, limits=None) -> np.ndarray:
         """Forward of the row positions ``rows`` of one sequence x [L], whose queries attend
         to the positions ``keys`` only (``rows`` must be among them).
 
         Every position keeps its own index as its rotary position.  With
         ``keys = range(L)`` this is the full-context forward; a shorter ``keys``
         is the pruned context of approximate suffix pruning (the positions not in
-        ``keys`` are absent for the model).  K/V of the rows are written to the
-        cache at their positions first.  Returns the final hidden states of the
-        rows, [len(rows), d].
+        ``keys`` are absent for the model).  ``limits`` (one per row) narrows each
+        row's keys further to the positions below its limit (block-causal
+        attention).  K/V of the rows are written to the cache at their positions
+        first.  Returns the final hidden states of the rows, [len(rows), d].
         """
         cfg = self.cfg
         eps = cfg["rms_eps"]
@@ -176,7 +197,11 @@ class Model:
             k = apply_rope(k, cos, sin)
             ck[l][rows] = k
             cv[l][rows] = v
-            o = attention(q, ck[l][keys], cv[l][keys]).reshape(n, self.H * self.hd)
+            if limits is None:
+                o = attention(q, ck[l][keys], cv[l][keys])
+            else:
+                o = attention_limited(q, ck[l][keys], cv[l][keys], keys, limits)
+            o = o.reshape(n, self.H * self.hd)
             h = h + o @ self._W(p + "wo").T
             f = rms_norm(h, self._W(p + "ffn_norm"), eps)
             h = h + swiglu_ffn(f, self._W(p + "w_gate"), self._W(p + "w_up"),

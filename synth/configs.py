@@ -38,7 +38,7 @@ NO_CACHE, PREFIX_CACHE, DUAL_CACHE = 0, 1, 2
 
 _COMMON = dict(rms_eps=1e-5, rope_base=10000.0, logit_scale=20.0, steps=0, threshold=0.9,
                weight_seed=1234, prompt_seed=5678, weight_std=0.02, random_gains=False,
-               suffix_window=-1)
+               suffix_window=-1, attention="full")
 
 CONFIGS = {
     # Tiny LLaDA-style model in fp32.

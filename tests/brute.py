@@ -41,9 +41,10 @@ class Brute:
         self.K = [[[None] * Hkv for _ in range(self.L)] for _ in range(nl)]
         self.V = [[[None] * Hkv for _ in range(self.L)] for _ in range(nl)]
 
-    def forward_rows(self, x, rows, pos=None):
+    def forward_rows(self, x, rows, pos=None, limit=None):
         """Forward of indices ``rows`` of the token list x; index i sits at rotary position
-        pos[i] (default i).  Every query attends to all len(x) indices."""
+        pos[i] (default i).  A query at index p attends to indices m < limit(p) (default all
+        len(x) indices)."""
         cfg = self.cfg
         H, Hkv, hd, eps = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["rms_eps"]
         W = self.W
@@ -66,12 +67,13 @@ class Brute:
                 o = []
                 for j in range(H):
                     g = j * Hkv // H
+                    nk = n if limit is None else limit(p)
                     sc = [sum(qs[p][j][t] * self.K[l][m][g][t] for t in range(hd)) / math.sqrt(hd)
-                          for m in range(n)]
+                          for m in range(nk)]
                     mx = max(sc)
                     e = [math.exp(v - mx) for v in sc]
                     tot = sum(e)
-                    o += [sum(e[m] / tot * self.V[l][m][g][t] for m in range(n)) for t in range(hd)]
+                    o += [sum(e[m] / tot * self.V[l][m][g][t] for m in range(nk)) for t in range(hd)]
                 hs[p] = [a + b for a, b in zip(hs[p], _matvec(W[pre + "wo"], o))]
                 f = _rms(hs[p], W[pre + "ffn_norm"], eps)
                 gt = _matvec(W[pre + "w_gate"], f)
@@ -101,6 +103,8 @@ class Brute:
         x = list(prompt) + [mask] * G
         steps = []
         win = cfg.get("suffix_window", -1)
+        if cfg.get("attention", "full") == "block_causal":
+            return self._generate_block_causal(x)
         for b in range(nb):
             s, e = P + b * Bs, P + (b + 1) * Bs
             # suffix pruning: the model runs on the shorter sequence of the kept positions
@@ -119,6 +123,36 @@ class Brute:
                 else:
                     rows = list(range(s, e))
                 hs = self.forward_rows([x[p] for p in keep], rows, keep)
+                st = {p: self.stats(hs[p]) for p in range(s, e)}
+                k = max(1, Bs // spb + (1 if j < Bs % spb else 0))
+                masked = [p for p in range(s, e) if x[p] == mask]
+                ranking = sorted(masked, key=lambda p: (-st[p][1], p))
+                n_above = sum(1 for p in masked if st[p][1] > cfg["threshold"])
+                chosen = ranking[:max(k, n_above)]
+                for p in chosen:
+                    x[p] = st[p][0]
+                steps.append(dict(block=b, j=j, stats=st, chosen=sorted(chosen)))
+                j += 1
+        return x, steps
+
+    def _generate_block_causal(self, x):
+        """Block-causal decoding spelled without a cache: every step recomputes every position
+        up to the block's end from scratch, a query at p attending to the indices below the end
+        of p's block (the prompt being one block)."""
+        cfg = self.cfg
+        P, G, Bs, mask = cfg["prompt_len"], cfg["gen_length"], cfg["block_size"], cfg["mask_id"]
+        nb = G // Bs
+        spb = (cfg["steps"] or G) // nb
+
+        def block_end(p):
+            return P if p < P else P + ((p - P) // Bs + 1) * Bs
+
+        steps = []
+        for b in range(nb):
+            s, e = P + b * Bs, P + (b + 1) * Bs
+            j = 0
+            while any(x[i] == mask for i in range(s, e)):
+                hs = self.forward_rows(x[:e], list(range(e)), None, block_end)
                 st = {p: self.stats(hs[p]) for p in range(s, e)}
                 k = max(1, Bs // spb + (1 if j < Bs % spb else 0))
                 masked = [p for p in range(s, e) if x[p] == mask]
