@@ -162,6 +162,8 @@ def main():
                     help="skip the event-instrumented pass (roofline and kernel classes)")
     ap.add_argument("--suffix-window", type=int, default=None,
                     help="approximate suffix pruning window (default: the workload's, -1 = off)")
+    ap.add_argument("--attention", choices=["full", "block_causal"], default=None,
+                    help="attention pattern (default: the workload's, full)")
     ap.add_argument("--blocks", type=int, default=0,
                     help="time prefill plus only the first N blocks (default: the whole generate)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -192,6 +194,8 @@ def main():
     cfg = synth.configs.get(args.workload)
     if args.suffix_window is not None:
         cfg["suffix_window"] = args.suffix_window
+    if args.attention is not None:
+        cfg["attention"] = args.attention
     nb_all = cfg["gen_length"] // cfg["block_size"]
     nblocks = args.blocks if 0 < args.blocks < nb_all else nb_all
     torch.cuda.set_device(0)
@@ -248,6 +252,7 @@ def main():
     out = {
         "metric": ("committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)"
                    if cfg["name"] == "llada8b" and cfg["suffix_window"] < 0 and nblocks == nb_all
+                   and cfg["attention"] == "full"
                    else f"committed tokens/s ({cfg['name']})"),
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
@@ -257,7 +262,8 @@ def main():
                    "batch": B, "prompt_len": cfg["prompt_len"], "gen_length": G,
                    "block_size": cfg["block_size"], "threshold": cfg["threshold"],
                    "use_cache": ["none", "prefix", "dual"][cfg["use_cache"]],
-                   "suffix_window": cfg["suffix_window"], "blocks_timed": nblocks},
+                   "suffix_window": cfg["suffix_window"], "attention": cfg["attention"],
+                   "blocks_timed": nblocks},
         "roofline": roof,
         "denoise_steps_per_generate": st["steps"],
         "refreshes_per_generate": st["full_forwards"],

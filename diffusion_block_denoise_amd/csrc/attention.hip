@@ -17,6 +17,9 @@
 // in chunk order.
 //
 // f32 path: one workgroup per (query row, head): scores in LDS, then weights times V.
+//
+// Every kernel lets a query see the keys below rs.key_limit of its slot: the context length,
+// or with block-causal attention the end of the query's block.
 #include "kernels.h"
 
 namespace dllm {
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   const int head = g * G + (valid ? r % G : 0);
   const int m = b * rs.nR + pi;
   const int ldq = H * HD;
+  const int klim = rs.key_limit(rs.start + pi);  // keys this lane's query may see
 
   // Q^T as the B operand: lane = query column, 8 dims per k-step.
   bf16x8_t qh[KS], ql[KS];
@@ -137,18 +141,19 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
-      s[i] = key < rs.L ? s[i] * scale_log2 : -INFINITY;
+      s[i] = key < klim ? s[i] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, s[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
     // P^T as hi/lo B operands of the next product; register i of k-step i/8 holds key slot i%8.
+    // (A lane with no visible key yet has mnew = -inf: its probabilities are 0, not NaN.)
     bf16x8_t ph[2], pl[2];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pv = exp2f(s[i] - mnew);
+      const float pv = mnew == -INFINITY ? 0.f : exp2f(s[i] - mnew);
       const __bf16 hi = (__bf16)pv;
       ph[i >> 3][i & 7] = hi;
       pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
@@ -255,6 +260,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
   const int head = g * G + (valid ? r % G : 0);
   const int m = b * rs.nR + pi;
   const int ldq = H * HD;
+  const int klim = rs.key_limit(rs.start + pi);  // keys this lane's query may see
 
   bf16x8_t qh[KS], ql[KS];
 #pragma unroll
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
-      sc[i] = key < rs.L ? sc[i] * scale_log2 : -INFINITY;
+      sc[i] = key < klim ? sc[i] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, sc[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pv = exp2f(sc[i] - mnew);
+      const float pv = mnew == -INFINITY ? 0.f : exp2f(sc[i] - mnew);
       const __bf16 hi = (__bf16)pv;
       ph[i >> 3][i & 7] = hi;
       pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
@@ -433,8 +439,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   const float *K = kc + ((size_t)b * Hkv + g) * rs.Lp * hd;
   const float *V = vt + ((size_t)b * Hkv + g) * hd * rs.Lp;
   const int lane = threadIdx.x;
+  const int nk = rs.key_limit(rs.start + m % rs.nR);  // keys this query may see
   float mx = -INFINITY;
-  for (int key = lane; key < rs.L; key += 64) {
+  for (int key = lane; key < nk; key += 64) {
     float s = 0.f;
     for (int d = 0; d < hd; ++d) s = fmaf(qr[d], K[(size_t)key * hd + d], s);
     s *= scale;
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   float sum = 0.f;
-  for (int key = lane; key < rs.L; key += 64) {
+  for (int key = lane; key < nk; key += 64) {
     const float p = expf(sc[key] - mx);
     sc[key] = p;
     sum += p;
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
   for (int d = lane; d < hd; d += 64) {
     float acc = 0.f;
     const float *vr = V + (size_t)d * rs.Lp;
-    for (int key = 0; key < rs.L; ++key) acc = fmaf(sc[key], vr[key], acc);
+    for (int key = 0; key < nk; ++key) acc = fmaf(sc[key], vr[key], acc);
     o[(size_t)m * H * hd + head * hd + d] = acc / sum;
   }
 }

@@ -74,6 +74,7 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
   const int steps = c->steps ? c->steps : c->gen_length;
   if (steps % nb) return bad("steps must be a multiple of gen_length/block_size (%d)", nb);
   if (std::isnan(c->threshold)) return bad("threshold is NaN");
+  if (c->attention < 0 || c->attention > 1) return bad("attention must be 0 (full) or 1 (block-causal)");
   if (c->use_cache < 0 || c->use_cache > 2) return bad("use_cache must be 0, 1 or 2");
   const long long L = (long long)c->prompt_len + c->gen_length;
   if (L * c->batch > (1LL << 26)) return bad("batch * (prompt_len + gen_length) too large");
@@ -86,7 +87,8 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
 // Workspace plan
 struct Plan {
   int B, P, G, Bs, L, Lp, NB, spb, d, H, Hkv, hd, F, V, nq, nkv, dt;
-  int W;  // suffix window (< 0: whole context)
+  int W;       // suffix window (< 0: whole context)
+  int causal;  // block-causal attention
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
@@ -103,6 +105,7 @@ RowSet rows_of(const Plan &p, int start, int nR) {
   RowSet r;
   r.B = p.B; r.L = p.L; r.Lp = p.Lp; r.start = start; r.nR = nR;
   r.Lx = p.L; r.tail = -1;
+  r.causal = p.causal; r.P = p.P; r.Bs = p.Bs;
   return r;
 }
 
@@ -111,6 +114,10 @@ RowSet rows_of(const Plan &p, int start, int nR) {
 // position in slot e + W; the whole sequence when W < 0 or the window reaches the end.
 int context_len(const Plan &p, int b, int *tail) {
   const int e = p.P + (b + 1) * p.Bs;
+  if (p.causal) {  // block-causal: nothing after the block is visible to anyone
+    *tail = -1;
+    return e;
+  }
   if (p.W < 0 || e + p.W >= p.L - 1) {
     *tail = -1;
     return p.L;
@@ -134,12 +141,14 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.F = c->ffn_dim; p.V = c->vocab; p.nq = p.H * p.hd; p.nkv = p.Hkv * p.hd;
   p.dt = c->dtype == DLLM_BF16 ? 1 : 0;
   p.W = c->suffix_window;
+  p.causal = c->attention == DLLM_ATTN_BLOCK_CAUSAL ? 1 : 0;
   const size_t Mmax = (size_t)p.B * p.L;
   p.Mmax = Mmax;
   p.kv_layer_elems = (size_t)p.B * p.Hkv * p.Lp * p.hd;
 
   // Row counts that a forward can have: refresh / no cache (B*L, or B*Lc_b with suffix
-  // pruning), dual step (B*Bs), prefix step of block b (B*(L - s_b) or B*(Lc_b - s_b)).
+  // pruning, or two blocks with block-causal attention), dual step (B*Bs), prefix step of
+  // block b (B*(L - s_b) or B*(Lc_b - s_b)).
   std::vector<int> Ms = {p.B * p.L, p.B * p.Bs};
   for (int b = 0; b < p.NB; ++b) {
     int tail;
@@ -147,6 +156,7 @@ void make_plan(const dllm_cfg *c, Plan &p) {
     Ms.push_back(p.B * (p.L - s0));
     Ms.push_back(p.B * Lc);
     Ms.push_back(p.B * (Lc - s0));
+    if (p.causal) Ms.push_back(p.B * (b > 0 ? 2 * p.Bs : p.P + p.Bs));  // block-causal refresh
   }
   size_t gpart = 0, apart = 0;
   for (int M : Ms) {
@@ -501,8 +511,12 @@ int head(dllm_t *h) {
 
 int refresh(dllm_t *h) {
   int tail;
-  const int Lc = context_len(h->p, h->block, &tail);
-  int rc = forward(h, rows_in_context(h->p, h->block, 0, Lc));
+  const Plan &p = h->p;
+  const int Lc = context_len(p, h->block, &tail);
+  // block-causal: only the previous block (its tokens are now final; for block 0 the prompt)
+  // and the current block; every earlier K/V is final
+  const int r0 = p.causal && h->block > 0 ? p.P + (h->block - 1) * p.Bs : 0;
+  int rc = forward(h, rows_in_context(p, h->block, r0, Lc - r0));
   if (rc) return rc;
   h->stats.full_forwards++;
   return head(h);

@@ -24,8 +24,17 @@ struct RowSet {
   int nR;     // rows per batch row
   int Lx;     // token-state length per batch row (prompt + generation)
   int tail;   // slot that holds position Lx - 1, or -1
+  // block-causal attention: a query at position p sees keys below the end of p's block (the
+  // prompt, P positions, is one block; then blocks of Bs)
+  int causal, P, Bs;
   __host__ __device__ int M() const { return B * nR; }
   __host__ __device__ int pos(int c) const { return c == tail ? Lx - 1 : c; }
+  // keys [0, key_limit(c)) are visible to the query in slot c
+  __host__ __device__ int key_limit(int c) const {
+    if (!causal) return L;
+    const int e = c < P ? P : P + ((c - P) / Bs + 1) * Bs;
+    return e < L ? e : L;
+  }
 };
 
 // GEMM epilogues.  The GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (fp32 accumulate).

@@ -32,7 +32,8 @@ class dllm_cfg(C.Structure):
                 ("batch", C.c_int32), ("prompt_len", C.c_int32), ("gen_length", C.c_int32),
                 ("block_size", C.c_int32), ("steps", C.c_int32), ("threshold", C.c_float),
                 ("use_cache", C.c_int32), ("refresh_every_step", C.c_int32),
-                ("suffix_window", C.c_int32), ("stream", C.c_void_p)]
+                ("suffix_window", C.c_int32), ("attention", C.c_int32),
+                ("stream", C.c_void_p)]
 
 
 class dllm_weights(C.Structure):
@@ -131,6 +132,7 @@ def make_cfg(cfg: dict, stream=None, refresh_every_step: bool = False) -> dllm_c
     c.dtype = DLLM_BF16 if cfg["dtype"] == "bf16" else DLLM_F32
     c.refresh_every_step = 1 if refresh_every_step else 0
     c.suffix_window = int(cfg.get("suffix_window", -1))
+    c.attention = {"full": 0, "block_causal": 1}[cfg.get("attention", "full")]
     c.stream = stream
     return c
 

@@ -52,6 +52,10 @@ extern "C" {
 #define DLLM_F32 0
 #define DLLM_BF16 1
 
+/* Attention pattern (attention). */
+#define DLLM_ATTN_FULL 0         /* bidirectional over the whole context (v1)          */
+#define DLLM_ATTN_BLOCK_CAUSAL 1 /* a query sees its own block and the ones before it   */
+
 /* Cache policy (use_cache). */
 #define DLLM_NO_CACHE 0     /* every step is a full forward                      */
 #define DLLM_PREFIX_CACHE 1 /* steps recompute the block and every later row      */
@@ -81,6 +85,12 @@ extern "C" {
  *   is decoded the model sees only positions [0, e + suffix_window) and the
  *   last position, each at its own rotary position, for the block's refresh
  *   and its steps; the other suffix positions are absent.  < 0: whole context.
+ *   attention = DLLM_ATTN_BLOCK_CAUSAL (block diffusion: Fast-dLLM README track
+ *   table, v2 "Block Diffusion"; Streaming-dLLM README, note on block-causal
+ *   models): the prompt is one block, then blocks of block_size; a query sees
+ *   its own block and every earlier one.  Finished blocks' K/V are final, so the
+ *   refresh at block b recomputes only blocks b-1 (the prompt for b = 0) and b,
+ *   and use_cache / suffix_window change nothing.
  *   All batch rows share prompt_len and advance block by block together.
  */
 typedef struct dllm_cfg {
@@ -93,7 +103,8 @@ typedef struct dllm_cfg {
   int32_t use_cache;
   int32_t refresh_every_step;
   int32_t suffix_window;
-  void *stream; /* hipStream_t */
+  int32_t attention; /* DLLM_ATTN_* */
+  void *stream;      /* hipStream_t */
 } dllm_cfg;
 
 /*

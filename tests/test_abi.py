@@ -39,8 +39,8 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu %zu\\n", sizeof(dllm_cfg), offsetof(dllm_cfg, threshold),
          offsetof(dllm_cfg, stream), sizeof(dllm_weights), sizeof(dllm_stats));
-  printf("%zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
-         offsetof(dllm_cfg, suffix_window));
+  printf("%zu %zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
+         offsetof(dllm_cfg, suffix_window), offsetof(dllm_cfg, attention));
   return 0;
 }}
 """)
@@ -51,7 +51,7 @@ int main(void) {{
     want = [C.sizeof(dllm.dllm_cfg), dllm.dllm_cfg.threshold.offset, dllm.dllm_cfg.stream.offset,
             C.sizeof(dllm.dllm_weights), C.sizeof(dllm.dllm_stats),
             dllm.dllm_stats.commits_hist.offset, dllm.dllm_stats.ms_step.offset,
-            dllm.dllm_cfg.suffix_window.offset]
+            dllm.dllm_cfg.suffix_window.offset, dllm.dllm_cfg.attention.offset]
     assert got == want
 
 
@@ -85,7 +85,7 @@ BAD = [
     ("dtype", 7), ("n_layers", 0), ("n_heads", 6), ("head_dim", 48), ("mask_id", 512),
     ("mask_id", -1), ("vocab", 1), ("gen_length", 60), ("block_size", 0), ("block_size", 512),
     ("steps", 6), ("steps", -4), ("use_cache", 3), ("batch", 0), ("prompt_len", -1),
-    ("threshold", float("nan")), ("rms_eps", -1.0), ("rope_base", 0.0),
+    ("threshold", float("nan")), ("rms_eps", -1.0), ("rope_base", 0.0), ("attention", 2),
 ]
 
 
