@@ -275,7 +275,7 @@ def main():
                            for k, v in prof.items()},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg["attention"] == "full":  # the sample is a full-context one
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(cfg, W, st["full_forwards"], st["cached_forwards"],
                                            tokens)
