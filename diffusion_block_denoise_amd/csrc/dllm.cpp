@@ -163,10 +163,7 @@ void make_plan(const dllm_cfg *c, Plan &p) {
     const int bn = gemm_bn(M, p.dt);
     const int ffn_virtual = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
     const int shapes[4][2] = {{p.nq + 2 * p.nkv, p.d}, {p.d, p.nq}, {ffn_virtual, p.d}, {p.d, p.F}};
-    for (auto &s : shapes) {
-      const int splits = gemm_num_splits(M, s[0], s[1], p.dt);
-      if (splits > 1) gpart = std::max(gpart, (size_t)splits * M * s[0] * sizeof(float));
-    }
+    for (auto &s : shapes) gpart = std::max(gpart, gemm_partial_bytes(M, s[0], s[1], p.dt));
     const int nR = M / p.B;
     apart = std::max(apart, attention_part_bytes(rows_of(p, 0, nR), p.H, p.Hkv, p.hd, p.dt));
   }
@@ -174,8 +171,7 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   {
     const int M = p.B * p.Bs, bn = gemm_bn(M, p.dt);
     p.n_vtiles = (p.V + bn - 1) / bn;
-    const int splits = gemm_num_splits(M, p.V, p.d, p.dt);
-    if (splits > 1) gpart = std::max(gpart, (size_t)splits * M * p.V * sizeof(float));
+    gpart = std::max(gpart, gemm_partial_bytes(M, p.V, p.d, p.dt));
   }
 
   // packed copies of the bf16 linear weights (the GEMM W layout)

@@ -16,6 +16,12 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
+#include <vector>
 #include <float.h>
 #include <limits.h>
 
@@ -234,33 +240,37 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
   }
 }
 
-// Split-K: each split writes its tile to partial[split][M][N]; a reduce kernel sums the splits
-// in split order (deterministic) and runs the epilogue.  No cross-workgroup fence: on a
-// multi-XCD GPU an agent-scope release fence writes back the XCD's L2, which costs far more
+// Split-K: each split writes its tile to partial[split][M][N - n_tail0]; a reduce kernel sums
+// the splits in split order (deterministic) and runs the epilogue.  No cross-workgroup fence: on
+// a multi-XCD GPU an agent-scope release fence writes back the XCD's L2, which costs far more
 // than the separate launch.
 template <int BM, int BN>
-__device__ void write_partial(const GemmArgs &a, const float *Ct, int ldc, int m0, int n0) {
-  float *P = a.partial + (size_t)blockIdx.z * a.M * a.N;
+__device__ void write_partial(const GemmArgs &a, int split, const float *Ct, int ldc, int m0,
+                              int n0) {
+  const int ld = a.N - a.n_tail0;
+  float *P = a.partial + (size_t)split * a.M * ld - a.n_tail0;
   for (int e = threadIdx.x; e < BM * BN; e += NT) {
     const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
-    if (m < a.M && n < a.N) P[(size_t)m * a.N + n] = Ct[r * ldc + c];
+    if (m < a.M && n < a.N) P[(size_t)m * ld + n] = Ct[r * ldc + c];
   }
 }
 
 static constexpr int RD_BM = 8, RD_BN = 128;
 
 // Tile reduce for the epilogues that need a whole tile (rotary pairs, gate/up halves, lm_head
-// softmax partials): 8 x 128 tiles, 4 consecutive columns per thread.
+// softmax partials): 8 x 128 tiles of the columns from n_tail0 on, 4 consecutive columns per
+// thread.
 __global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int splits) {
   constexpr int LDC = RD_BN + 4;
   __shared__ float Ct[RD_BM * LDC];
-  const int m0 = blockIdx.y * RD_BM, n0 = blockIdx.x * RD_BN;
-  const size_t MN = (size_t)a.M * a.N;
+  const int m0 = blockIdx.y * RD_BM, n0 = a.n_tail0 + blockIdx.x * RD_BN;
+  const int ld = a.N - a.n_tail0;
+  const size_t MN = (size_t)a.M * ld;
   const int r = threadIdx.x / (RD_BN / 4), c = (threadIdx.x % (RD_BN / 4)) * 4;
   const int m = m0 + r, n = n0 + c;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (m < a.M && n < a.N) {  // N is a multiple of 4 (widths are multiples of 64)
-    const float *p = a.partial + (size_t)m * a.N + n;
+    const float *p = a.partial + (size_t)m * ld + (n - a.n_tail0);
     for (int z = 0; z < splits; ++z) {
       const float4 v = *(const float4 *)(p + z * MN);
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
@@ -272,6 +282,18 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int s
 }
 
 // ---------------------------------------------------------------------------------------------
+// Tile t -> (M tile, N tile): groups of GM rows of M tiles, M tile index fastest inside a group.
+// The workgroups resident at one time then share a few A row blocks and a few W panels, so both
+// stay in the caches when A is too large for them (a refresh of many batch rows).  With at most
+// GM rows of M tiles this is plain M-fastest order: a column's tiles are consecutive.
+__device__ inline void tile_coords(int t, int mt, int nt, int gm, int &tm, int &tn) {
+  const int g = t / (gm * nt), r = t - g * gm * nt;
+  const int rows = min(gm, mt - g * gm);
+  tm = g * gm + r % rows;
+  tn = r / rows;
+}
+static constexpr int TILED_GM = 16, BIG_GM = 8;
+
 // Tiled bf16 MFMA kernel for many rows (block refresh).  4 waves as WM x WN; each wave owns
 // (BM/WM) x (BN/WN) of the tile in 32x32 blocks (v_mfma_f32_32x32x16_bf16).  BK = 64.
 template <int BM, int BN, int WM, int WN>
@@ -290,9 +312,21 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kbeg = blockIdx.z * a.k_split;
-  const int kend = min(a.K, kbeg + a.k_split);
+  // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
+  // split covers whole columns and every row of a column is summed in the same order) and K range
+  const int w = blockIdx.x, mt = (a.M + BM - 1) / BM;
+  int tile = w, split = -1, kbeg = 0, kend = a.K;
+  if (w >= a.n_full) {
+    const int j = w - a.n_full;
+    tile = a.n_full + j / a.tail_sp;
+    split = j % a.tail_sp;
+    kbeg = split * a.k_split;
+    kend = min(a.K, kbeg + a.k_split);
+    if (a.tail_sp == 1) split = -1;
+  }
+  int tm, tn;
+  tile_coords(tile, mt, (a.N + BN - 1) / BN, TILED_GM, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
 
   // Global -> register staging: 16-byte chunks, 8 per 64-wide row.  Native vector types: arrays
   // of HIP's uint4 struct defeat register promotion and end up in scratch memory.
@@ -357,6 +391,8 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
     store();
     __syncthreads();
     load(min(k0 + BK, kend - BK));
+    // keep the next tile's loads ahead of the MFMAs (the scheduler would sink them to the store)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t fa_hi[TM], fa_lo[TM], fb[TN];
@@ -394,11 +430,176 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
         Ct[row * LDC + col] = acc[i][j][r];
       }
   __syncthreads();
-  if (gridDim.z > 1) {
-    write_partial<BM, BN>(a, Ct, LDC, m0, n0);
+  if (split >= 0) {
+    write_partial<BM, BN>(a, split, Ct, LDC, m0, n0);
     return;
   }
   run_epilogue<bf16, BM, BN>(a, Ct, LDC, m0, n0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Large-tile bf16 MFMA kernel for many rows (block refresh of long contexts and batches).  A
+// workgroup of 4 waves owns a 256 x 256 tile; each wave a 128 x 128 quadrant as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (256 accumulator registers), so every fragment read from LDS feeds 4
+// (A) or 8 (W, hi and lo) MFMAs.  K advances in stages of 32 through a ring of 3 LDS slots
+// filled straight from global memory (global_load_lds, 16 bytes per lane, no register staging),
+// 2 stages ahead; one barrier per stage.  In a slot, a [rows][32] region holds row r's 16-byte
+// chunk c at chunk position 4 r + (c ^ ((r >> 1) & 3)): 8 consecutive rows of one chunk column
+// then cover all 32 banks, so the fragment reads are conflict-free.
+static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NS = 3;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline int bg_pos(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+
+__global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
+  constexpr int REG = BG_BM * BG_BK * 2;     // one [256][32] bf16 region: 16 KB
+  constexpr int STAGE = 3 * REG;             // A hi, A lo, W
+  constexpr int LDC = 2 * 128 + 4;           // epilogue: 128 rows x 256 columns of fp32
+  static_assert(128 * LDC * 4 <= BG_NS * STAGE, "epilogue tile must fit the ring");
+  __shared__ __align__(1024) unsigned char smem[BG_NS * STAGE];
+  float *Ct = (float *)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // work item -> tile and K range, as in gemm_mfma_kernel
+  const int w = blockIdx.x, mt = (a.M + BG_BM - 1) / BG_BM;
+  int tile = w, split = -1, kbeg = 0, kend = a.K;
+  if (w >= a.n_full) {
+    const int j = w - a.n_full;
+    tile = a.n_full + j / a.tail_sp;
+    split = j % a.tail_sp;
+    kbeg = split * a.k_split;
+    kend = min(a.K, kbeg + a.k_split);
+    if (a.tail_sp == 1) split = -1;
+  }
+  int tm, tn;
+  tile_coords(tile, mt, (a.N + BG_BN - 1) / BG_BN, BIG_GM, tm, tn);
+  const int m0 = tm * BG_BM, n0 = tn * BG_BN;
+  const int T = (kend - kbeg) / BG_BK;
+
+  // Loads: wave w's instruction j (0..3) of each region fills chunk positions (4 w + j) * 64 +
+  // lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 1) & 3).  Rows past M read
+  // row M - 1 and panels past the last one read the last one (their outputs are never written).
+  const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
+  size_t aoff[4];
+  const uint16_t *wsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pos = (wave * 4 + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 1) & 3);
+    aoff[j] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda + c * 8;
+    wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
+  }
+  const uint16_t *ahi = (const uint16_t *)a.a_hi, *alo = (const uint16_t *)a.a_lo;
+  // stage t -> slot t % 3; past the last stage the loads re-read it (clamped, unused), so every
+  // iteration has the same number of loads in flight
+  auto issue = [&](int t) {
+    const int k0 = kbeg + min(t, T - 1) * BG_BK;
+    unsigned char *st = smem + (t % BG_NS) * STAGE + wave * 4096;
+    const size_t kw = (size_t)(k0 / PW_K) * (PW_ROWS * PW_K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds((const void *)(ahi + aoff[j] + k0), (lds_void *)(st + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(alo + aoff[j] + k0), (lds_void *)(st + REG + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(wsrc[j] + kw), (lds_void *)(st + 2 * REG + j * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment rows: lane l reads row (l & 31) of each 32-row block, chunk kk * 2 + (l >> 5)
+  const int frow = lane & 31, fsw = (frow >> 1) & 3, fhalf = lane >> 5;
+  const int arow = (wm * 128 + frow) * 64, wrow = (wn * 128 + frow) * 64;
+  // Fragments are double-buffered per 16-wide k step: the reads of the next step go out before
+  // the MFMAs of the current one.
+  bf16x8_t fh[2][4], fl[2][4], fb[2][4];
+  auto read_frags = [&](int t, int kk, int buf) {
+    const unsigned char *st = smem + (t % BG_NS) * STAGE;
+    const int cb = ((kk * 2 + fhalf) ^ fsw) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fh[buf][i] = *(const bf16x8_t *)(st + arow + i * 2048 + cb);
+      fl[buf][i] = *(const bf16x8_t *)(st + REG + arow + i * 2048 + cb);
+      fb[buf][i] = *(const bf16x8_t *)(st + 2 * REG + wrow + i * 2048 + cb);
+    }
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Stage t's loads are issued at stage t - 3 (the prologue issues 0..2) into slot t % 3, which
+  // every wave has finished reading at the barrier of stage t - 2's second half.  Past the last
+  // stage the loads and reads repeat clamped addresses (unused), so the wait counts are static.
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24): stage 0 has landed
+  barrier();
+  read_frags(0, 0, 0);
+  for (int t = 0; t < T; ++t) {
+    // at most 12 reads outstanding at a time (the LDS counter only counts to 15)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): buffer 0 is in registers
+    read_frags(t, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage t + 1 has landed once only stage t + 2's 12 loads are outstanding; all of this
+    // wave's reads of stage t are complete before the barrier
+    __builtin_amdgcn_s_waitcnt(0x007C);  // vmcnt(12) lgkmcnt(0)
+    barrier();
+    issue(t + 3);  // into the slot of stage t
+    read_frags(min(t + 1, T - 1), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the ring
+  __syncthreads();
+  // Epilogue in two row halves: the waves of half h write their 128 x 128 quadrants into a
+  // 128 x 256 C tile, then all threads run the 128 x 128 epilogue on each column half.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
+            Ct[row * LDC + wn * 128 + j * 32 + frow] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (split >= 0)
+        write_partial<128, 128>(a, split, Ct + q * 128, LDC, m0 + h * 128, n0 + q * 128);
+      else
+        run_epilogue<bf16, 128, 128>(a, Ct + q * 128, LDC, m0 + h * 128, n0 + q * 128);
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -521,7 +722,7 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
         Ct[(i * 16 + 4 * g + r) * LDC + wave * 32 + cb * 16 + rn] = acc[i][cb][r];
   __syncthreads();
   if (gridDim.z > 1) {
-    write_partial<BM, SK_BN>(a, Ct, LDC, 0, n0);
+    write_partial<BM, SK_BN>(a, blockIdx.z, Ct, LDC, 0, n0);
     return;
   }
   run_epilogue<bf16, BM, SK_BN>(a, Ct, LDC, 0, n0);
@@ -575,49 +776,177 @@ static bool use_skinny(int M, int K) { return M <= 64 && K % SK_KA == 0; }
 
 static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16) : 128; }
 
-// Split-K plan.  Skinny kernel: as many splits as keep the grid within one round of resident
-// workgroups (3 per CU up to 32 rows, 2 up to 48, 1 at 64), at least 512 k per split and at
-// most 8 splits (more only adds partial traffic).  Tiled kernel: see below.
-static void split_plan(int M, int N, int K, int dtype, int &splits, int &kc) {
-  splits = 1;
-  kc = K;
-  if (dtype == 0) return;
-  const bool sk = use_skinny(M, K);
-  const int bm = bm_for(M, K), bn = gemm_bn(M, dtype);
-  const long tiles = (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int unit = sk ? SK_KA : 64;  // split lengths are whole stages / K steps
-  int want, max_splits;
-  if (sk) {
-    const long cap = (M <= 32 ? 3 : (M <= 48 ? 2 : 1)) * 256L;
-    want = (int)(cap / tiles);
-    max_splits = std::min(K / 512, 8);
-  } else {
-    // Estimated time (us): rounds of resident workgroups (2 per CU) times the K steps of a
-    // split at ~1.8 us per step and round, plus the round trip of the fp32 partial tiles
-    // (written here, read by the reduce) at ~5 TB/s when split.  At most 16 splits of at
-    // least 4 K steps.  (Fitted to the 768-row projections of the 8B shape on MI355X.)
-    const int iters = K / 64;
-    const long slots = 512;
-    double best = 1e30;
-    want = 1;
-    for (int sp = 1; sp <= 16 && sp <= std::max(1, iters / 4); ++sp) {
-      const long rounds = (tiles * sp + slots - 1) / slots;
-      const double partial_us = sp > 1 ? sp * (double)M * N * 8.0 / 5.0e6 : 0.0;
-      const double cost = 1.8 * rounds * ((iters + sp - 1) / sp) + partial_us;
-      if (cost < best - 1e-9) { best = cost; want = sp; }
+// Kernel and split-K plan.
+//   Skinny kernel (M <= 64): as many splits as keep the grid within one round of resident
+//   workgroups (3 per CU up to 32 rows, 2 up to 48, 1 at 64), at least 512 k per split and at
+//   most 8 splits (more only adds partial traffic); every tile is split alike.
+//   Tiled (128 x 128) and large-tile (256 x 256) kernels: the first n_full work items are whole
+//   tiles (whole columns of M tiles) and the remaining columns are split tail_sp ways, so that
+//   the last, partly filled round of resident workgroups is spread over the whole GPU.  The plan
+//   minimises an estimate of the time: the work items, in launch order, placed on the 256 CUs
+//   (cu_makespan), plus the round trip of the fp32 partial tiles (written here, read by the
+//   reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted on MI355X to the 8B-shape
+//   projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K step of 64 alone on its
+//   CU and 1.98 us when two share it (they are limited by the CU, not by latency); a 256 x 256
+//   workgroup (one per CU) 4.0 us.  The large-tile kernel serves M >= 2048 when its tiles fill at
+//   least one round.
+enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3 };
+
+struct SplitPlan {
+  int kind;     // GemmKind
+  int splits;   // skinny: gridDim.z; tiled / large-tile: tail_sp
+  int kc;       // K per split
+  int n_full;   // tiled / large-tile: whole-tile work items
+  int n_tail0;  // first split column
+};
+
+// Estimated time (us) of n_full items of it_full K steps followed by n_tail items of it_tail
+// steps on `cus` CUs holding up to per_cu workgroups each.  Items are handed out in launch order
+// to the least occupied CUs (round-robin at the start).  A workgroup alone on its CU takes t1 us
+// per K step, each of two sharing a CU t2.
+static double cu_makespan(long n_full, int it_full, long n_tail, int it_tail, int cus, int per_cu,
+                          double t1, double t2) {
+  struct Cu { double last; int n; double rem[2]; int ver; };
+  std::vector<Cu> cu(cus, Cu{0.0, 0, {0.0, 0.0}, 0});
+  const long total = n_full + n_tail;
+  long next = 0;
+  auto step_time = [&](const Cu &u) { return u.n == 1 ? t1 : t2; };
+  auto advance = [&](Cu &u, double T) {  // progress to time T, drop finished items
+    if (u.n) {
+      const double done = (T - u.last) / step_time(u);
+      int k = 0;
+      for (int i = 0; i < u.n; ++i)
+        if (u.rem[i] - done > 1e-9) u.rem[k++] = u.rem[i] - done;
+      u.n = k;
     }
-    max_splits = std::max(1, K / 256);
+    u.last = T;
+  };
+  typedef std::pair<double, int> Ev;
+  std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> q;
+  std::vector<int> qver(cus, -1);
+  auto schedule = [&](int c) {
+    Cu &u = cu[c];
+    ++u.ver;
+    if (!u.n) return;
+    double m = u.rem[0];
+    for (int i = 1; i < u.n; ++i) m = std::min(m, u.rem[i]);
+    q.push(Ev(u.last + m * step_time(u), c * 4096 + (u.ver & 4095)));
+  };
+  auto dispatch = [&](double T) {
+    for (int want = 0; want < per_cu && next < total; ++want)
+      for (int c = 0; c < cus && next < total; ++c) {
+        Cu &u = cu[c];
+        if (u.n != want) continue;
+        advance(u, T);
+        if (u.n != want) continue;
+        u.rem[u.n++] = next < n_full ? it_full : it_tail;
+        ++next;
+        schedule(c);
+      }
+  };
+  dispatch(0.0);
+  double end = 0.0;
+  while (!q.empty()) {
+    const double T = q.top().first;
+    while (!q.empty() && q.top().first <= T + 1e-9) {
+      const int c = q.top().second / 4096, v = q.top().second % 4096;
+      q.pop();
+      if (v != (cu[c].ver & 4095)) continue;  // superseded
+      advance(cu[c], T);
+      schedule(c);
+    }
+    end = std::max(end, T);
+    dispatch(T);
   }
+  return end;
+}
+
+static SplitPlan tile_plan(int kind, int M, int N, int K) {
+  const bool big = kind == GK_BIG;
+  const int bm = big ? 256 : 128, bn = big ? 256 : 128, per_cu = big ? 1 : 2;
+  const double t1 = big ? 4.0 : 1.25, t2 = 1.98;
+  const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn, iters = K / 64;
+  const long tiles = (long)mt * nt;
+  SplitPlan best_plan{kind, 1, K, (int)tiles, N};
+  // splits need whole columns in launch order: a single group of rows (tile_coords); with many
+  // rounds of tiles the tail is negligible
+  if (mt > (big ? BIG_GM : TILED_GM) || tiles > 16L * 256 * per_cu) return best_plan;
+  double best = 1e30;
+  // candidate full-column counts: none, or whole rounds of resident workgroups
+  const int cands[2] = {0, (int)((tiles / (256 * per_cu)) * (256 * per_cu) / mt)};
+  for (int ci = 0; ci < 2; ++ci) {
+    const int c = std::min(cands[ci], nt);
+    if (ci == 1 && c == 0) continue;
+    const long n_full = (long)c * mt, n_tail_tiles = tiles - n_full;
+    const int max_sp = n_tail_tiles == 0 ? 1 : std::min(16, std::max(1, iters / 4));
+    for (int sp = 1; sp <= max_sp; ++sp) {
+      const int kc = ((K + sp - 1) / sp + 63) / 64 * 64, splits = (K + kc - 1) / kc;
+      if (splits != sp) continue;
+      const double span = cu_makespan(n_full, iters, n_tail_tiles * splits, kc / 64, 256, per_cu, t1, t2);
+      const int tail_cols = N - c * bn;
+      const double partial_us = splits > 1 ? splits * (double)M * tail_cols * 8.0 / 6.0e6 + 4.0 : 0.0;
+      const double cost = span + partial_us;
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_plan = SplitPlan{kind, splits, kc, (int)n_full, splits > 1 ? c * bn : N};
+      }
+    }
+  }
+  if (best_plan.splits == 1) { best_plan.n_full = (int)tiles; best_plan.n_tail0 = N; }
+  return best_plan;
+}
+
+static int choose_kind(int M, int N, int K, int dtype) {
+  if (dtype == 0) return GK_F32;
+  if (use_skinny(M, K)) return GK_SKINNY;
+  const long big_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (M >= 2048 && big_tiles >= 256 && K % 64 == 0) return GK_BIG;
+  return GK_TILED;
+}
+
+// The tile plans are computed once per shape (the list schedule takes up to a few ms).
+static SplitPlan tile_plan_cached(int kind, int M, int N, int K) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int>, SplitPlan> cache;
+  const auto key = std::make_tuple(kind, M, N, K);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const SplitPlan pl = tile_plan(kind, M, N, K);
+  std::lock_guard<std::mutex> lk(mu);
+  cache.emplace(key, pl);
+  return pl;
+}
+
+static SplitPlan split_plan(int M, int N, int K, int dtype) {
+  const int kind = choose_kind(M, N, K, dtype);
+  SplitPlan pl{kind, 1, K, 0, 0};
+  if (kind == GK_F32) return pl;
+  if (kind != GK_SKINNY) return tile_plan_cached(kind, M, N, K);
+  const long tiles = (N + SK_BN - 1) / SK_BN;  // one 16..64-row tile in M
+  const long cap = (M <= 32 ? 3 : (M <= 48 ? 2 : 1)) * 256L;
+  int want = (int)(cap / tiles);
+  const int max_splits = std::min(K / 512, 8);
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;
-  kc = ((K + want - 1) / want + unit - 1) / unit * unit;
-  splits = (K + kc - 1) / kc;
+  pl.kc = ((K + want - 1) / want + SK_KA - 1) / SK_KA * SK_KA;
+  pl.splits = (K + pl.kc - 1) / pl.kc;
+  return pl;
 }
 
 int gemm_num_splits(int M, int N, int K, int dtype) {
-  int splits, kc;
-  split_plan(M, N, K, dtype, splits, kc);
-  return splits;
+  const SplitPlan pl = split_plan(M, N, K, dtype);
+  // tiled kernels with whole tiles first: the tail is reduced inside launch_gemm
+  if (pl.kind != GK_SKINNY && pl.n_full > 0) return 1;
+  return pl.splits;
+}
+
+size_t gemm_partial_bytes(int M, int N, int K, int dtype) {
+  const SplitPlan pl = split_plan(M, N, K, dtype);
+  if (pl.splits <= 1) return 0;
+  return (size_t)pl.splits * M * (N - pl.n_tail0) * sizeof(float);
 }
 
 int gemm_kind(int M, int K, int dtype) {
@@ -639,24 +968,45 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     return hipGetLastError();
   }
-  const int bm = bm_for(a.M, a.K), bn = gemm_bn(a.M, dtype);
-  int splits, kc;
-  split_plan(a.M, a.N, a.K, dtype, splits, kc);
-  a.k_split = kc;
-  if (splits_out) *splits_out = splits;
-  dim3 grid((a.N + bn - 1) / bn, (a.M + bm - 1) / bm, splits);
-  switch (bm) {
-    case 16: hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(NT), 0, st, a); break;
-    case 32: hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(NT), 0, st, a); break;
-    case 48: hipLaunchKernelGGL(gemm_skinny_kernel<3>, grid, dim3(NT), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(NT), 0, st, a); break;
-    default: hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), grid, dim3(NT), 0, st, a);
+  const SplitPlan pl = split_plan(a.M, a.N, a.K, dtype);
+  a.k_split = pl.kc;
+  static_assert(RD_BN == SK_BN, "reduce tiles must match the GEMM's column tiles");
+  if (use_skinny(a.M, a.K)) {
+    a.n_full = 0; a.tail_sp = 1; a.n_tail0 = 0;
+    if (splits_out) *splits_out = pl.splits;
+    const int bm = bm_for(a.M, a.K);
+    dim3 grid((a.N + SK_BN - 1) / SK_BN, 1, pl.splits);
+    switch (bm) {
+      case 16: hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(NT), 0, st, a); break;
+      case 32: hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(NT), 0, st, a); break;
+      case 48: hipLaunchKernelGGL(gemm_skinny_kernel<3>, grid, dim3(NT), 0, st, a); break;
+      default: hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(NT), 0, st, a); break;
+    }
+    if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+    if (pl.splits > 1 && a.epi != EPI_RESID) {
+      dim3 rgrid((a.N + RD_BN - 1) / RD_BN, (a.M + RD_BM - 1) / RD_BM);
+      hipLaunchKernelGGL(gemm_reduce_kernel, rgrid, dim3(NT), 0, st, a, pl.splits);
+    }
+    return hipGetLastError();
   }
+  const int bt = pl.kind == GK_BIG ? 256 : 128;
+  const int mt = (a.M + bt - 1) / bt, nt = (a.N + bt - 1) / bt;
+  a.n_full = pl.n_full;
+  a.tail_sp = pl.splits;
+  a.n_tail0 = pl.n_tail0;
+  const long items = (long)pl.n_full + ((long)mt * nt - pl.n_full) * pl.splits;
+  if (pl.kind == GK_BIG)
+    hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), dim3((unsigned)items), dim3(NT), 0, st, a);
   if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
-  if (splits > 1 && a.epi != EPI_RESID) {
-    static_assert(RD_BN == SK_BN, "reduce tiles must match the GEMM's column tiles");
-    dim3 rgrid((a.N + RD_BN - 1) / RD_BN, (a.M + RD_BM - 1) / RD_BM);
-    hipLaunchKernelGGL(gemm_reduce_kernel, rgrid, dim3(NT), 0, st, a, splits);
+  if (pl.splits > 1) {
+    if (pl.n_full == 0 && a.epi == EPI_RESID) {
+      if (splits_out) *splits_out = pl.splits;  // the caller folds the partials
+    } else {
+      dim3 rgrid((a.N - pl.n_tail0 + RD_BN - 1) / RD_BN, (a.M + RD_BM - 1) / RD_BM);
+      hipLaunchKernelGGL(gemm_reduce_kernel, rgrid, dim3(NT), 0, st, a, pl.splits);
+    }
   }
   return hipGetLastError();
 }

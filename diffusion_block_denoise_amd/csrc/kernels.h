@@ -75,8 +75,13 @@ struct GemmArgs {
   const uint16_t *wp;
   int n_half;     // SwiGLU: ffn_dim
   int M, N, K;    // N is the virtual width (SwiGLU: 2 * ceil(ffn_dim / (BN/2)) * (BN/2))
-  int k_split;    // K elements per split (multiple of the kernel's BK); gridDim.z splits
-  float *partial; // split-K partial tiles [splits][M][N] fp32 (when gridDim.z > 1)
+  int k_split;    // K elements per split (multiple of the kernel's BK)
+  // Split-K partial tiles fp32 [splits][M][N - n_tail0]: column n of a split tile is stored at
+  // column n - n_tail0.  Skinny kernel: gridDim.z splits of every tile, n_tail0 = 0.  Tiled
+  // kernel (1-D grid, M-tile index fastest): work items below n_full are whole tiles with their
+  // epilogue; each later tile (all of them columns from n_tail0 on) is split tail_sp ways.
+  float *partial;
+  int n_full, tail_sp, n_tail0;
   int epi;
   // epilogue operands
   float *out_f32; int ld_out; float scale;        // STORE
@@ -115,7 +120,10 @@ int gemm_kind(int M, int K, int dtype);
 // Tile width (N direction) that launch_gemm uses for a given M and dtype; SwiGLU and
 // the lm_head partial layout depend on it.
 int gemm_bn(int M, int dtype);
+// Splits of the caller-visible partial buffer (EPI_RESID folds them in resid_norm), and the
+// partial buffer size in bytes that launch_gemm needs for this shape.
 int gemm_num_splits(int M, int N, int K, int dtype);
+size_t gemm_partial_bytes(int M, int N, int K, int dtype);
 
 // h[m] = embed[x[b][p]] (fp32); a = RMSNorm(h[m]) * gain as hi/lo planes (bf16) or f32.
 hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rows, int d,
