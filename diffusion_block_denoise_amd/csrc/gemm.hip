@@ -617,7 +617,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
 // split length are multiples of SK_KA).
 static constexpr int SK_BN = 128, SK_KA = 256, SK_D = SK_KA / 64;
 
-template <int MT>
+// NS > 0: the workgroup's K range is exactly NS stages and the stage loop is unrolled, which
+// lets the compiler count the loads in flight exactly (with a loop it drains every load at the
+// top of each stage); NS = 0: any number of stages.
+template <int MT, int NS>
 __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
   constexpr int BM = 16 * MT;
   constexpr int LDA = SK_KA + 8;
@@ -637,7 +640,7 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
   const int kbeg = blockIdx.z * a.k_split;
   const int kend = min(a.K, kbeg + a.k_split);
   const int nchunk = (kend - kbeg) / 64;
-  const int nstage = (nchunk + SK_D - 1) / SK_D;
+  const int nstage = NS > 0 ? NS : (nchunk + SK_D - 1) / SK_D;
 
   // W rows of this lane in the packed panel n0/128 (rows past N are zero-padded)
   static_assert(SK_BN == PW_ROWS, "one panel per workgroup");
@@ -687,6 +690,8 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
   load_a(0);
 #pragma unroll
   for (int sl = 0; sl < SK_D; ++sl) load_w(sl, sl);
+  constexpr int UNROLL = NS > 0 ? NS : 1;
+#pragma unroll UNROLL
   for (int st = 0; st < nstage; ++st) {
     store_a();
     __syncthreads();
@@ -777,9 +782,9 @@ static bool use_skinny(int M, int K) { return M <= 64 && K % SK_KA == 0; }
 static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16) : 128; }
 
 // Kernel and split-K plan.
-//   Skinny kernel (M <= 64): as many splits as keep the grid within one round of resident
-//   workgroups (3 per CU up to 32 rows, 2 up to 48, 1 at 64), at least 512 k per split and at
-//   most 8 splits (more only adds partial traffic); every tile is split alike.
+//   Skinny kernel (M <= 64): the fewest power-of-two splits (every tile split alike) that give
+//   at least 192 workgroups, with whole stages per split; if K has too few factors of two, as
+//   many stage-aligned splits as reach 192 workgroups (or one stage each).
 //   Tiled (128 x 128) and large-tile (256 x 256) kernels: the first n_full work items are whole
 //   tiles (whole columns of M tiles) and the remaining columns are split tail_sp ways, so that
 //   the last, partly filled round of resident workgroups is spread over the whole GPU.  The plan
@@ -926,11 +931,12 @@ static SplitPlan split_plan(int M, int N, int K, int dtype) {
   if (kind == GK_F32) return pl;
   if (kind != GK_SKINNY) return tile_plan_cached(kind, M, N, K);
   const long tiles = (N + SK_BN - 1) / SK_BN;  // one 16..64-row tile in M
-  const long cap = (M <= 32 ? 3 : (M <= 48 ? 2 : 1)) * 256L;
-  int want = (int)(cap / tiles);
-  const int max_splits = std::min(K / 512, 8);
-  if (want > max_splits) want = max_splits;
-  if (want < 1) want = 1;
+  // the fewest power-of-two splits that give at least 192 workgroups (3/4 of the CUs): more
+  // splits add partial traffic and, for the epilogues that need whole sums, a reduce launch
+  int want = 1;
+  while (tiles * want < 192 && want < 16 && K % (2 * want * SK_KA) == 0) want *= 2;
+  // K not divisible that far: uneven splits of whole stages (the last one shorter)
+  if (tiles * want < 192) want = (int)std::min<long>((192 + tiles - 1) / tiles, std::max(1, K / SK_KA));
   pl.kc = ((K + want - 1) / want + SK_KA - 1) / SK_KA * SK_KA;
   pl.splits = (K + pl.kc - 1) / pl.kc;
   return pl;
@@ -976,12 +982,26 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
     if (splits_out) *splits_out = pl.splits;
     const int bm = bm_for(a.M, a.K);
     dim3 grid((a.N + SK_BN - 1) / SK_BN, 1, pl.splits);
+    // unrolled variants when every split has the same whole number of stages
+    const int ns = (a.K % pl.kc == 0) ? pl.kc / SK_KA : 0;
+#define SKINNY_NS(MT_)                                                                         \
+  switch (ns) {                                                                                \
+    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 1>), grid, dim3(NT), 0, st, a); break;   \
+    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 2>), grid, dim3(NT), 0, st, a); break;   \
+    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 3>), grid, dim3(NT), 0, st, a); break;   \
+    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 4>), grid, dim3(NT), 0, st, a); break;   \
+    case 6: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 6>), grid, dim3(NT), 0, st, a); break;   \
+    case 8: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 8>), grid, dim3(NT), 0, st, a); break;   \
+    case 16: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 16>), grid, dim3(NT), 0, st, a); break; \
+    default: hipLaunchKernelGGL((gemm_skinny_kernel<MT_, 0>), grid, dim3(NT), 0, st, a); break;  \
+  }
     switch (bm) {
-      case 16: hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(NT), 0, st, a); break;
-      case 32: hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(NT), 0, st, a); break;
-      case 48: hipLaunchKernelGGL(gemm_skinny_kernel<3>, grid, dim3(NT), 0, st, a); break;
-      default: hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(NT), 0, st, a); break;
+      case 16: SKINNY_NS(1) break;
+      case 32: SKINNY_NS(2) break;
+      case 48: SKINNY_NS(3) break;
+      default: SKINNY_NS(4) break;
     }
+#undef SKINNY_NS
     if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
     if (pl.splits > 1 && a.epi != EPI_RESID) {
       dim3 rgrid((a.N + RD_BN - 1) / RD_BN, (a.M + RD_BM - 1) / RD_BM);
