@@ -28,6 +28,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+static constexpr int ATTN_MAX_SPLITS = 16;  // key chunks of one query tile (merge width)
+
 static inline int attn_tiles(RowSet rs, int H, int Hkv) {
   return (rs.nR * (H / Hkv) + 31) / 32;
 }
@@ -37,6 +39,7 @@ static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk)
   const int kt = (rs.L + 31) / 32;  // 32-key tiles of the context
   int want = (int)((256 + waves - 1) / waves);
   if (want > kt) want = kt;
+  if (want > ATTN_MAX_SPLITS) want = ATTN_MAX_SPLITS;
   if (want < 1) want = 1;
   chunk = (kt + want - 1) / want * 32;
   splits = (kt * 32 + chunk - 1) / chunk;
@@ -403,25 +406,46 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict_
   const int m = b * rs.nR + r / G, head = g * G + r % G;
   const size_t stride = (size_t)rs.B * Hkv * n_qt * 32 * (HD + 2);
   const float *p0 = part + (((size_t)bg * n_qt + qt) * 32 + col) * (HD + 2);
+  // lane s holds chunk s's running max and sum; every load of the merge is issued before the
+  // first one is used (one memory latency instead of one per chunk), and the sums still run in
+  // chunk order
+  const int lane = threadIdx.x;
+  float m_own = -INFINITY, l_own = 0.f;
+  if (lane < splits) {
+    m_own = p0[lane * stride + HD];
+    l_own = p0[lane * stride + HD + 1];
+  }
+  constexpr int DPL = (HD + 63) / 64;  // dims per lane (lanes past HD idle when HD < 64)
+  const bool dim_ok = lane < HD;
+  float v[ATTN_MAX_SPLITS][DPL];
+#pragma unroll
+  for (int s = 0; s < ATTN_MAX_SPLITS; ++s)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) v[s][j] = (s < splits && dim_ok) ? p0[s * stride + lane + 64 * j] : 0.f;
   float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, p0[s * stride + HD]);
-  float l = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = p0[s * stride + HD];
-    if (ms > -INFINITY) l += p0[s * stride + HD + 1] * exp2f(ms - mx);
+#pragma unroll
+  for (int s = 0; s < ATTN_MAX_SPLITS; ++s)
+    if (s < splits) mx = fmaxf(mx, __shfl(m_own, s, 64));
+  float l = 0.f, w[ATTN_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < ATTN_MAX_SPLITS; ++s) {
+    const float ms = __shfl(m_own, s, 64), ls = __shfl(l_own, s, 64);
+    w[s] = (s < splits && ms > -INFINITY) ? exp2f(ms - mx) : 0.f;
+    if (s < splits && ms > -INFINITY) l += ls * w[s];
   }
   const float inv = 1.0f / l;
-  for (int dim = threadIdx.x; dim < HD; dim += 64) {
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) {
     float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = p0[s * stride + HD];
-      if (ms > -INFINITY) acc += p0[s * stride + dim] * exp2f(ms - mx);
-    }
-    const float v = acc * inv;
-    const size_t o = (size_t)m * H * HD + head * HD + dim;
-    const bf16 hi = __float2bfloat16(v);
+#pragma unroll
+    for (int s = 0; s < ATTN_MAX_SPLITS; ++s)
+      if (w[s] != 0.f) acc += v[s][j] * w[s];
+    const float val = acc * inv;
+    if (!dim_ok) break;
+    const size_t o = (size_t)m * H * HD + head * HD + lane + 64 * j;
+    const bf16 hi = __float2bfloat16(val);
     o_hi[o] = hi;
-    o_lo[o] = __float2bfloat16(v - __bfloat162float(hi));
+    o_lo[o] = __float2bfloat16(val - __bfloat162float(hi));
   }
 }
 
