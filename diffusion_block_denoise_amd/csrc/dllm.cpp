@@ -92,7 +92,7 @@ struct Plan {
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
-      off_ncom, off_rem, off_wpack, total;
+      off_ncom, off_rem, off_wpack, off_hc, off_qc, total;
   // packed bf16 weights (elements): per layer QKV, Wo, gate/up, down, then the lm_head
   int n_gu;  // virtual gate/up width (64 gate + 64 up rows per 128-row panel)
   size_t wp_qkv, wp_o, wp_gu, wp_down, wp_layer, wp_lm;
@@ -210,6 +210,9 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_com = take((size_t)p.B * p.Bs);
   p.off_ncom = take((size_t)p.B * 4);
   p.off_rem = take((size_t)p.B * 4);
+  // the block rows' residual stream and queries in the last layer (forward)
+  p.off_hc = take((size_t)p.B * p.Bs * p.d * 4);
+  p.off_qc = take((size_t)p.B * p.Bs * p.nq * 4);
   p.total = o;
 }
 
@@ -228,6 +231,8 @@ struct dllm_handle {
   int *x;
   char *kc, *vc;
   float *cos_t, *sin_t, *h;
+  float *hc;  // block rows' residual stream in the last layer
+  void *qc;   // block rows' queries in the last layer (fp32, or bf16 hi plane + lo plane)
   void *a_hi, *a_lo, *act_hi, *act_lo, *q;
   float *apart, *gpart;
   HeadPart *hpart;
@@ -369,9 +374,9 @@ GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M
   return g;
 }
 
-void set_resid(dllm_t *h, GemmArgs &g) {
+void set_resid(dllm_t *h, GemmArgs &g, float *hres) {
   g.epi = EPI_RESID;
-  g.resid = h->h;
+  g.resid = hres;
   g.ld_out = h->p.d;
 }
 
@@ -382,28 +387,36 @@ int resid_gemm_norm(dllm_t *h, GemmArgs &g, const void *gain) {
   int splits = 1;
   int rc = run_gemm(h, g, g.N, 8.0 * g.M * g.N, &splits);  // h read and written
   if (rc) return rc;
-  HIPCHK(launch_resid_norm(g.M, p.d, h->h, splits > 1 ? h->gpart : nullptr, splits > 1 ? splits : 0,
+  HIPCHK(launch_resid_norm(g.M, p.d, g.resid, splits > 1 ? h->gpart : nullptr, splits > 1 ? splits : 0,
                            gain, h->cfg.rms_eps, bf ? (bf16 *)h->a_hi : nullptr,
                            bf ? (bf16 *)h->a_lo : nullptr, bf ? nullptr : (float *)h->a_hi, p.dt,
                            h->st));
   return DLLM_OK;
 }
 
-// One forward over row set rs.  Afterwards h holds the final residual stream and a holds
-// RMSNorm(h) with the final-norm gain (the lm_head input).
+// One forward over row set rs.  Every layer's K/V are written for all rows of rs, but only the
+// current block's rows feed the lm_head: after the last layer's Q/K/V projection the forward
+// continues with the block rows alone (their queries and residual stream gathered into hc and
+// qc).  Afterwards a holds RMSNorm(h) with the final-norm gain for the rows h->last_rows.
 int forward(dllm_t *h, RowSet rs) {
   const Plan &p = h->p;
   const dllm_cfg &c = h->cfg;
-  const int M = rs.M();
   const bool bf = p.dt == 1;
   bf16 *ahi = (bf16 *)h->a_hi, *alo = (bf16 *)h->a_lo;
   float *af = (float *)h->a_hi;
   HIPCHK(launch_embed_norm(h->x, h->embed, LW(h, 0, 0), rs, p.d, c.rms_eps, h->h, bf ? ahi : nullptr,
                            bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+  const int s_blk = p.P + h->block * p.Bs;
+  const bool narrow = h->block >= 0 && !(rs.start == s_blk && rs.nR == p.Bs) &&
+                      rs.start <= s_blk && s_blk + p.Bs <= rs.start + rs.nR;
+  RowSet lrs = rs;  // rows carried through the rest of the current layer
+  float *hres = h->h;
+  void *qb = h->q;
   for (int l = 0; l < c.n_layers; ++l) {
+    const int Mq = rs.M();
     // Q, K, V projections of a; rotary embedding; K/V to the cache slots of rows rs
     {
-      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, p.nq + 2 * p.nkv, p.d);
+      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, Mq, p.nq + 2 * p.nkv, p.d);
       g.w[0] = LW(h, l, 1); g.w[1] = LW(h, l, 2); g.w[2] = LW(h, l, 3);
       g.seg_end[0] = p.nq; g.seg_end[1] = p.nq + p.nkv; g.seg_end[2] = p.nq + 2 * p.nkv;
       g.wp = WP(h, l, 0);
@@ -418,18 +431,35 @@ int forward(dllm_t *h, RowSet rs) {
         g.k_cache_lo = kv_layer_lo(h, h->kc, l);
         g.vt_cache_lo = kv_layer_lo(h, h->vc, l);
       }
-      int rc = run_gemm(h, g, g.N, 4.0 * M * g.N, nullptr);  // q, K, V as 4-byte pairs
+      int rc = run_gemm(h, g, g.N, 4.0 * Mq * g.N, nullptr);  // q, K, V as 4-byte pairs
       if (rc) return rc;
     }
+    if (l == c.n_layers - 1 && narrow) {
+      // last layer: only the block rows go on (their K/V, and everyone else's, are written)
+      lrs = rs;
+      lrs.start = s_blk;
+      lrs.nR = p.Bs;
+      const int off = s_blk - rs.start, n = p.Bs;
+      const size_t qrow = (size_t)p.nq * (bf ? 2 : 4);
+      HIPCHK(launch_gather_rows(h->q, h->qc, p.B, n, rs.nR, off, qrow, h->st));
+      if (bf)
+        HIPCHK(launch_gather_rows(q_lo(h), (char *)h->qc + (size_t)p.B * n * qrow, p.B, n, rs.nR,
+                                  off, qrow, h->st));
+      HIPCHK(launch_gather_rows(h->h, h->hc, p.B, n, rs.nR, off, (size_t)p.d * 4, h->st));
+      hres = h->hc;
+      qb = h->qc;
+    }
+    const int M = lrs.M();
+    const void *qb_lo = bf ? (qb == h->q ? q_lo(h) : (char *)h->qc + (size_t)M * p.nq * 2) : nullptr;
     // attention over all cached positions -> a (input of the output projection)
     {
       hipEvent_t eb, ee;
       int rc = prof_events(h, DLLM_KC_ATTENTION, &eb, &ee);
       if (rc) return rc;
       if (eb) HIPCHK(hipEventRecord(eb, h->st));
-      HIPCHK(launch_attention(h->q, bf ? q_lo(h) : nullptr, kv_layer(h, h->kc, l),
+      HIPCHK(launch_attention(qb, qb_lo, kv_layer(h, h->kc, l),
                               bf ? kv_layer_lo(h, h->kc, l) : nullptr, kv_layer(h, h->vc, l),
-                              bf ? kv_layer_lo(h, h->vc, l) : nullptr, rs, p.H, p.Hkv, p.hd,
+                              bf ? kv_layer_lo(h, h->vc, l) : nullptr, lrs, p.H, p.Hkv, p.hd,
                               bf ? ahi : nullptr, bf ? alo : nullptr, bf ? nullptr : af, h->apart,
                               p.dt, h->st));
       if (ee) {
@@ -445,7 +475,7 @@ int forward(dllm_t *h, RowSet rs) {
       GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.nq, M, p.d, p.nq);
       g.w[0] = LW(h, l, 4); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
       g.wp = WP(h, l, 1);
-      set_resid(h, g);
+      set_resid(h, g, hres);
       int rc = resid_gemm_norm(h, g, LW(h, l, 5));
       if (rc) return rc;
     }
@@ -469,12 +499,12 @@ int forward(dllm_t *h, RowSet rs) {
       GemmArgs g = gemm_base(h, h->act_hi, h->act_lo, p.F, M, p.d, p.F);
       g.w[0] = LW(h, l, 8); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
       g.wp = WP(h, l, 3);
-      set_resid(h, g);
+      set_resid(h, g, hres);
       int rc = resid_gemm_norm(h, g, l + 1 < c.n_layers ? LW(h, l + 1, 0) : h->final_norm);
       if (rc) return rc;
     }
   }
-  h->last_rows = rs;
+  h->last_rows = lrs;
   h->any_forward = true;
   return DLLM_OK;
 }
@@ -652,6 +682,8 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->kc = ws + p.off_k; h->vc = ws + p.off_v;
   h->cos_t = (float *)(ws + p.off_cos); h->sin_t = (float *)(ws + p.off_sin);
   h->h = (float *)(ws + p.off_h);
+  h->hc = (float *)(ws + p.off_hc);
+  h->qc = ws + p.off_qc;
   h->a_hi = ws + p.off_ahi; h->a_lo = ws + p.off_alo;
   h->act_hi = ws + p.off_acthi; h->act_lo = ws + p.off_actlo;
   h->q = ws + p.off_q;

@@ -153,6 +153,10 @@ hipError_t launch_init_tokens(int *x, int B, int P, int L, int mask_id, hipStrea
 // cos/sin tables [L][hd/2] of theta = p * base^(-2i/hd), computed in fp64 on the device.
 hipError_t launch_rope_table(float *cos_t, float *sin_t, int L, int hd, float base, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t st);
+// dst row b * n + j = src row b * src_stride + src_off + j for b < B, j < n (rows of row_bytes,
+// a multiple of 16; src and dst must not overlap).
+hipError_t launch_gather_rows(const void *src, void *dst, int B, int n, int src_stride,
+                              int src_off, size_t row_bytes, hipStream_t st);
 // Mark the mask id column (-inf) of debug logits rows.
 hipError_t launch_mask_column(float *logits, int n_rows, int vocab, int mask_id, hipStream_t st);
 

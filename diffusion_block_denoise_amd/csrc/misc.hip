@@ -306,4 +306,26 @@ hipError_t launch_mask_column(float *logits, int n_rows, int vocab, int mask_id,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Row gather: dst row b * n + j = src row b * src_stride + src_off + j (b < B, j < n), rows of
+// row_bytes (a multiple of 16) bytes.  One workgroup per destination row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4 *__restrict__ src,
+                                                          uint4 *__restrict__ dst, int n,
+                                                          int src_stride, int src_off,
+                                                          int row_chunks) {
+  const int r = blockIdx.x, b = r / n, j = r % n;
+  const uint4 *s = src + ((size_t)b * src_stride + src_off + j) * row_chunks;
+  uint4 *d = dst + (size_t)r * row_chunks;
+  for (int c = threadIdx.x; c < row_chunks; c += 256) d[c] = s[c];
+}
+
+hipError_t launch_gather_rows(const void *src, void *dst, int B, int n, int src_stride,
+                              int src_off, size_t row_bytes, hipStream_t st) {
+  if (B <= 0 || n <= 0) return hipSuccess;
+  if (row_bytes % 16 || src_off < 0 || src_off + n > src_stride) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(B * n), dim3(256), 0, st, (const uint4 *)src,
+                     (uint4 *)dst, n, src_stride, src_off, (int)(row_bytes / 16));
+  return hipGetLastError();
+}
+
 }  // namespace dllm
