@@ -22,6 +22,8 @@
 // or with block-causal attention the end of the query's block.
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -45,12 +47,35 @@ static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk)
   splits = (kt * 32 + chunk - 1) / chunk;
 }
 
+// Many-query kernel (4 query tiles per workgroup, one workgroup per CU): split the keys only
+// when the workgroups fill less than half of the 256 CUs.  A workgroup's time per key tile
+// hardly changes with the number of workgroups (measured: 768 queries x 32 heads, 192
+// workgroups, 79 us whole; 4 chunks 70 us plus 21 us to merge), so splitting pays only when
+// most CUs would idle.
+static constexpr int AW_GROUP = 4;  // query tiles per workgroup (the kernel's waves)
+
+static inline void attn_wide_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk) {
+  const long wgs = (long)((attn_tiles(rs, H, Hkv) + AW_GROUP - 1) / AW_GROUP) * rs.B * Hkv;
+  const int kt = (rs.L + 31) / 32;
+  int want = wgs * 2 > 256 ? 1 : (int)std::min<long>(4, 256 / wgs);
+  want = std::max(1, std::min(want, kt / 2));
+  chunk = (kt + want - 1) / want * 32;
+  splits = (kt * 32 + chunk - 1) / chunk;
+}
+
 size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
   if (dtype == 0) return 0;
   int splits, chunk;
+  const int nqt = attn_tiles(rs, H, Hkv);
+  if (nqt >= AW_GROUP) {
+    attn_wide_plan(rs, H, Hkv, splits, chunk);
+    if (splits == 1) return 0;
+    const int n_qt = (nqt + AW_GROUP - 1) / AW_GROUP * AW_GROUP;
+    return (size_t)splits * rs.B * Hkv * n_qt * 32 * (hd + 2) * sizeof(float);
+  }
   attn_plan(rs, H, Hkv, splits, chunk);
   if (splits == 1) return 0;
-  return (size_t)splits * rs.B * Hkv * attn_tiles(rs, H, Hkv) * 32 * (hd + 2) * sizeof(float);
+  return (size_t)splits * rs.B * Hkv * nqt * 32 * (hd + 2) * sizeof(float);
 }
 
 template <int HD>
@@ -107,7 +132,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   // than two per tile.
   struct Tile {
     bf16x8_t kh[KS], kl[KS];
-    bf16x4_t vh[DB][2][2], vl[DB][2][2];
+    bf16x8_t vh[DB][2], vl[DB][2];
   };
   auto load_tile = [&](int kb, Tile &t) {
     const size_t krow = (size_t)(kb + col) * HD + half * 8;
@@ -118,14 +143,13 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     }
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
-      const size_t vrow = (size_t)(kb >> 5) * (HD * 32) + (d * 32 + col) * 32 + 4 * half;
+      // this lane's keys of 16-key step ks are chunk 2 ks + half of the tile row (vt_key_pos)
+      const size_t vrow = (size_t)(kb >> 5) * (HD * 32) + (d * 32 + col) * 32 + 8 * half;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          t.vh[d][ks][r] = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8 * r);
-          t.vl[d][ks][r] = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8 * r);
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        t.vh[d][ks] = *(const bf16x8_t *)(Vh + vrow + 16 * ks);
+        t.vl[d][ks] = *(const bf16x8_t *)(Vl + vrow + 16 * ks);
+      }
     }
   };
   auto compute_tile = [&](int kb, const Tile &t) {
@@ -165,21 +189,21 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     psum += __shfl_xor(psum, 32, 64);
     lsum = lsum * alpha + psum;
     mrun = mnew;
+    // rescale the running output only when some lane's maximum moved (alpha is exactly 1
+    // otherwise, so skipping changes nothing); after the first tiles it rarely moves
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-#pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t vh, vl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vh[e] = t.vh[d][ks][0][e]; vh[e + 4] = t.vh[d][ks][1][e];
-          vl[e] = t.vl[d][ks][0][e]; vl[e + 4] = t.vl[d][ks][1][e];
-        }
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vl[d][ks], ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], pl[ks], o[d], 0, 0, 0);
       }
     }
   };
@@ -227,33 +251,34 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 }
 
 // Many-query variant (block refresh): 4 waves per workgroup, one 32-query tile each, all of the
-// same (batch row, K/V head).  The 32-key tiles of K and V^T (hi and lo) are staged once per
-// workgroup in LDS, double-buffered with one barrier per tile, the next tile prefetched into
-// registers while the current one is used; every wave then runs the same MFMA sequence as the
-// per-wave kernel with its operands read from LDS.
-static constexpr int AW_WAVES = 4;
+// same (batch row, K/V head).  The 32-key tiles of K and V^T (hi and lo) go straight from global
+// memory into a ring of 3 LDS slots (global_load_lds, 16 bytes per lane, no register staging),
+// two tiles ahead, one barrier per tile; every wave runs the per-wave kernel's MFMA sequence
+// with its operands read from LDS.  In a slot, row r's 16-byte chunk c sits at chunk position
+// r * CPR + (c ^ f(r)) (CPR chunks per row; f(r) = r & 7 for rows of 8 or more chunks, else
+// (r >> 1) & 3), so the fragment reads of 8 consecutive rows hit distinct banks.  When the
+// workgroups cannot fill the GPU the keys are split into chunks (partials + the merge kernel).
+static constexpr int AW_WAVES = 4, AW_SLOTS = 3;
+
+__device__ inline int aw_swz(int r, int cpr) { return cpr >= 8 ? (r & 7) : ((r >> 1) & 3); }
 
 template <int HD>
-__global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
+__global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
-    RowSet rs, int H, int Hkv, float scale_log2, bf16 *o_hi, bf16 *o_lo) {
+    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part) {
   constexpr int KS = HD / 16, DB = HD / 32;
-  constexpr int KP = HD + 8;   // K tile row pitch (keys x dims), bf16 elements
-  constexpr int VP = 32 + 8;   // V^T tile row pitch (dims x keys)
-  constexpr int K_ELEMS = 32 * KP, V_ELEMS = HD * VP;
-  constexpr int STAGE = 2 * K_ELEMS + 2 * V_ELEMS;  // hi and lo of each
-  // 16-byte chunks per stage: K hi/lo 32*HD/8 each, V^T hi/lo HD*32/8 each
-  constexpr int CHUNKS = 4 * (32 * HD / 8);
-  constexpr int NTH = 64 * AW_WAVES;
-  constexpr int CPT = CHUNKS / NTH;  // chunks per thread
-  static_assert(CHUNKS % NTH == 0, "tile staging");
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  __shared__ __align__(16) uint16_t lds[2 * STAGE];
+  constexpr int PLANE = 32 * HD * 2;          // bytes of one plane of a 32-key tile
+  constexpr int SLOT = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
+  constexpr int LPW = SLOT / 1024 / AW_WAVES; // 1 KB loads per wave per tile
+  constexpr int KCPR = HD / 8, VCPR = 4;      // 16-byte chunks per K row / per V^T row
+  static_assert(SLOT % (1024 * AW_WAVES) == 0 && LPW >= 1, "tile staging");
+  typedef __attribute__((address_space(3))) void lds_void;
+  __shared__ __align__(1024) unsigned char lds[AW_SLOTS * SLOT];
 
   const int G = H / Hkv;
   const int nrows = rs.nR * G;
-  const int bg = blockIdx.y;
+  const int bg = blockIdx.y, split = blockIdx.z;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int qt = blockIdx.x * AW_WAVES + wave;
@@ -272,32 +297,32 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
     qh[kk] = *(const bf16x8_t *)(q_hi + o);  // invalid rows read row m of batch b: harmless
     ql[kk] = *(const bf16x8_t *)(q_lo + o);
   }
+  // K [Lp][HD]; V^T in 32-key tiles [Lp/32][HD][32]: tile kb of either plane starts kb * HD in
   const size_t kv_off = (size_t)bg * rs.Lp * HD;
-  const uint16_t *src[4] = {(const uint16_t *)k_hi + kv_off, (const uint16_t *)k_lo + kv_off,
-                            (const uint16_t *)vt_hi + kv_off, (const uint16_t *)vt_lo + kv_off};
-
-  // chunk c of a stage: plane = c / (32*HD/8); K planes: key c' / (HD/8), dims 8*(c' % (HD/8));
-  // V^T planes (a contiguous [HD][32] tile): dim c' / 4, keys 8*(c' % 4)
-  s16x8 pre[CPT];
-  auto load_tile = [&](int kb) {
+  // load j of this wave fills chunk positions (wave * LPW + j) * 64 + lane of the slot
+  const uint16_t *src[LPW];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NTH, plane = c / (32 * HD / 8), cc = c % (32 * HD / 8);
-      size_t off;
-      if (plane < 2) off = (size_t)(kb + cc / (HD / 8)) * HD + 8 * (cc % (HD / 8));
-      else off = (size_t)(kb >> 5) * (HD * 32) + 8 * cc;  // V^T tile: contiguous
-      pre[i] = *(const s16x8 *)(src[plane] + off);
+  for (int j = 0; j < LPW; ++j) {
+    const int e = (wave * LPW + j) * 64 + lane, plane = e / (PLANE / 16), pos = e % (PLANE / 16);
+    const bf16 *base = plane == 0 ? k_hi : plane == 1 ? k_lo : plane == 2 ? vt_hi : vt_lo;
+    int off;
+    if (plane < 2) {
+      const int rr = pos / KCPR, c = (pos % KCPR) ^ aw_swz(rr, KCPR);
+      off = rr * HD + c * 8;
+    } else {
+      const int rr = pos / VCPR, c = (pos % VCPR) ^ aw_swz(rr, VCPR);
+      off = rr * 32 + c * 8;
     }
-  };
-  auto store_tile = [&](uint16_t *st) {
+    src[j] = (const uint16_t *)base + kv_off + off;
+  }
+  const int ntile = (rs.L + 31) / 32;
+  const int t0 = split * (chunk / 32), t1 = min(ntile, t0 + chunk / 32), T = t1 - t0;
+  auto issue = [&](int u) {  // tile t0 + u (clamped to the last) into slot u % AW_SLOTS
+    const size_t kb = (size_t)(t0 + min(u, T - 1)) * 32;
+    unsigned char *dst = lds + (u % AW_SLOTS) * SLOT + wave * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NTH, plane = c / (32 * HD / 8), cc = c % (32 * HD / 8);
-      uint16_t *dst;
-      if (plane < 2) dst = st + plane * K_ELEMS + (cc / (HD / 8)) * KP + 8 * (cc % (HD / 8));
-      else dst = st + 2 * K_ELEMS + (plane - 2) * V_ELEMS + (cc / 4) * VP + 8 * (cc % 4);
-      *(s16x8 *)dst = pre[i];
-    }
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void *)(src[j] + kb * HD), (lds_void *)(dst + j * 1024), 16, 0, 0);
   };
 
   float mrun = -INFINITY, lsum = 0.f;
@@ -307,29 +332,54 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
 
-  const int ntile = (rs.L + 31) / 32;
-  load_tile(0);
-  store_tile(lds);
-  load_tile(min(1, ntile - 1) * 32);
-  for (int t = 0; t < ntile; ++t) {
-    __syncthreads();  // tile t in lds[t&1]; everyone is done with lds[(t+1)&1]
-    uint16_t *cur = lds + (t & 1) * STAGE;
-    if (t + 1 < ntile) store_tile(lds + ((t + 1) & 1) * STAGE);
-    load_tile(min(t + 2, ntile - 1) * 32);  // clamped: unconditional loads keep counts static
-    const int kb = t * 32;
-    const uint16_t *Kh = cur, *Kl = cur + K_ELEMS;
-    const uint16_t *Vh = cur + 2 * K_ELEMS, *Vl = Vh + V_ELEMS;
+  // fragment positions (bytes in a plane): K row col, chunk 2 kk + half; V^T row d * 32 + col,
+  // chunk 2 ks + half
+  const int ksw = aw_swz(col, KCPR), krow = col * KCPR;
+  issue(0);
+  issue(1);
+  for (int u = 0; u < T; ++u) {
+    // tile u has landed once only tile u + 1's loads are outstanding (vmcnt(LPW))
+    if constexpr (LPW == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if constexpr (LPW == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else __builtin_amdgcn_s_waitcnt(0x0F72);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's part of tile u is in LDS; tile u - 1 is done
+    asm volatile("" ::: "memory");
+    issue(u + 2);                  // into the slot of tile u - 1
+    const unsigned char *cur = lds + (u % AW_SLOTS) * SLOT;
+    const int kb = (t0 + u) * 32;
+    // all K fragments of the tile are read before the first MFMA, and all V^T fragments before
+    // the softmax, so each LDS latency is paid once per tile (the scheduler would otherwise wait
+    // on every pair of reads)
+    bf16x8_t kh[KS], kl[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int pos = (krow + ((kk * 2 + half) ^ ksw)) * 16;
+      kh[kk] = *(const bf16x8_t *)(cur + pos);
+      kl[kk] = *(const bf16x8_t *)(cur + PLANE + pos);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8_t kh = *(const bf16x8_t *)(Kh + col * KP + kk * 16 + half * 8);
-      const bf16x8_t kl = *(const bf16x8_t *)(Kl + col * KP + kk * 16 + half * 8);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kk], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kk], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], qh[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], sc, 0, 0, 0);
     }
+    bf16x8_t vfh[DB][2], vfl[DB][2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const int vr = d * 32 + col, vsw = aw_swz(vr, VCPR);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int pos = (vr * VCPR + ((ks * 2 + half) ^ vsw)) * 16;
+        vfh[d][ks] = *(const bf16x8_t *)(cur + 2 * PLANE + pos);
+        vfl[d][ks] = *(const bf16x8_t *)(cur + 3 * PLANE + pos);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -353,43 +403,53 @@ __global__ __launch_bounds__(64 * AW_WAVES) void attn_wide_kernel(
     psum += __shfl_xor(psum, 32, 64);
     lsum = lsum * alpha + psum;
     mrun = mnew;
+    // rescale the running output only when some lane's maximum moved (alpha is exactly 1
+    // otherwise, so skipping changes nothing); after the first tiles it rarely moves
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-      const int vrow = (d * 32 + col) * VP + 4 * half;
-#pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x4_t h0 = *(const bf16x4_t *)(Vh + vrow + 16 * ks);
-        const bf16x4_t h1 = *(const bf16x4_t *)(Vh + vrow + 16 * ks + 8);
-        const bf16x4_t l0 = *(const bf16x4_t *)(Vl + vrow + 16 * ks);
-        const bf16x4_t l1 = *(const bf16x4_t *)(Vl + vrow + 16 * ks + 8);
-        bf16x8_t vh, vl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vh[e] = h0[e]; vh[e + 4] = h1[e];
-          vl[e] = l0[e]; vl[e + 4] = l1[e];
-        }
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfl[d][ks], ph[ks], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], pl[ks], o[d], 0, 0, 0);
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
   if (!valid) return;
-  const float inv = 1.0f / lsum;
-  bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
-  bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
+  if (gridDim.z == 1) {
+    const float inv = 1.0f / lsum;
+    bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
+    bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
+    for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      const float v = o[d][i] * inv;
-      const bf16 hi = __float2bfloat16(v);
-      oh[dim] = hi;
-      ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+      for (int i = 0; i < 16; ++i) {
+        const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const float v = o[d][i] * inv;
+        const bf16 hi = __float2bfloat16(v);
+        oh[dim] = hi;
+        ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+      }
+  } else {
+    // part[split][bg][qt][col][HD + 2], as the few-query kernel writes it
+    const int n_qt = gridDim.x * AW_WAVES;
+    float *pp = part + ((((size_t)split * gridDim.y + bg) * n_qt + qt) * 32 + col) * (HD + 2);
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pp[d * 32 + 8 * (i >> 2) + 4 * half + (i & 3)] = o[d][i];
+    if (half == 0) {
+      pp[HD] = mrun;
+      pp[HD + 1] = lsum;
     }
+  }
 }
 
 // Combine the key chunks: one wave per query row slot, lanes over dims.
@@ -505,13 +565,21 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (nqt >= AW_WAVES) {
     // many queries: K/V tiles shared by the 4 waves of a workgroup through LDS
-    dim3 wgrid((nqt + AW_WAVES - 1) / AW_WAVES, rs.B * Hkv);
+    static_assert(AW_WAVES == AW_GROUP, "query tiles per workgroup");
+    int wsplits, wchunk;
+    attn_wide_plan(rs, H, Hkv, wsplits, wchunk);
+    const int groups = (nqt + AW_WAVES - 1) / AW_WAVES;
+    dim3 wgrid(groups, rs.B * Hkv, wsplits);
 #define ATTNW_CASE(HDV)                                                                          \
   case HDV:                                                                                      \
     hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES), 0, st, (const bf16 *)q, \
                        (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,      \
-                       (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv,            \
-                       scale_log2, o_hi, o_lo);                                                  \
+                       (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, wchunk,    \
+                       scale_log2, o_hi, o_lo, part);                                            \
+    if (wsplits > 1)                                                                             \
+      hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3(rs.B * Hkv * groups * AW_WAVES * 32),      \
+                         dim3(64), 0, st, (const float *)part, rs, H, Hkv, groups * AW_WAVES,    \
+                         wsplits, o_hi, o_lo);                                                   \
     break;
     switch (hd) {
       ATTNW_CASE(32)

@@ -176,9 +176,10 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
         } else {
           const int kvh = (n - nq - nk) / hd;
           // V^T per (batch row, K/V head): fp32 [hd][Lp]; bf16 in 32-key tiles [Lp/32][hd][32], so
-          // that the attention's key tile is one contiguous run per plane
+          // that the attention's key tile is one contiguous run per plane, with the keys of a tile
+          // ordered as the attention's probability operand holds them (vt_key_pos)
           const size_t base = ((size_t)b * Hkv + kvh) * hd * rs.Lp;
-          const size_t vi = sizeof(T) == 2 ? base + (size_t)(p >> 5) * hd * 32 + i * 32 + (p & 31)
+          const size_t vi = sizeof(T) == 2 ? base + (size_t)(p >> 5) * hd * 32 + i * 32 + vt_key_pos(p & 31)
                                            : base + (size_t)i * rs.Lp + p;
           store_val<T>(a.vt_cache, a.vt_cache_lo, vi, x);
         }

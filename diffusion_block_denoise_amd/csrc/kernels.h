@@ -37,6 +37,14 @@ struct RowSet {
   }
 };
 
+// Position of key k (0..31) inside a 32-key row of the bf16 V^T cache.  The P.V product's B
+// operand gives the lane of half h in 16-key step s the keys 16s + 4h + {0..3} and
+// 16s + 8 + 4h + {0..3}; storing them as the 16-byte chunk 2s + h lets the lane read its eight
+// V^T values with one load.
+__host__ __device__ inline int vt_key_pos(int k) {
+  return ((k >> 4) * 2 + ((k >> 2) & 1)) * 8 + ((k >> 3) & 1) * 4 + (k & 3);
+}
+
 // GEMM epilogues.  The GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (fp32 accumulate).
 enum Epi : int {
   EPI_STORE = 0,   // out_f32[m*ld_out + n] = scale * C
