@@ -315,7 +315,12 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
   // split covers whole columns and every row of a column is summed in the same order) and K range
-  const int w = blockIdx.x, mt = (a.M + BM - 1) / BM;
+  const int mt = (a.M + BM - 1) / BM;
+  int w = blockIdx.x;
+  if (w < a.xcd_cols * mt) {  // XCD-aware: the columns of XCD w % 8, M tiles in order
+    const int x = w & 7, k = w >> 3;
+    w = (x + 8 * (k / mt)) * mt + k % mt;
+  }
   int tile = w, split = -1, kbeg = 0, kend = a.K;
   if (w >= a.n_full) {
     const int j = w - a.n_full;
@@ -464,7 +469,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   // work item -> tile and K range, as in gemm_mfma_kernel
-  const int w = blockIdx.x, mt = (a.M + BG_BM - 1) / BG_BM;
+  const int mt = (a.M + BG_BM - 1) / BG_BM;
+  int w = blockIdx.x;
+  if (w < a.xcd_cols * mt) {  // XCD-aware: the columns of XCD w % 8, M tiles in order
+    const int x = w & 7, k = w >> 3;
+    w = (x + 8 * (k / mt)) * mt + k % mt;
+  }
   int tile = w, split = -1, kbeg = 0, kend = a.K;
   if (w >= a.n_full) {
     const int j = w - a.n_full;
@@ -979,7 +989,7 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   a.k_split = pl.kc;
   static_assert(RD_BN == SK_BN, "reduce tiles must match the GEMM's column tiles");
   if (use_skinny(a.M, a.K)) {
-    a.n_full = 0; a.tail_sp = 1; a.n_tail0 = 0;
+    a.n_full = 0; a.tail_sp = 1; a.n_tail0 = 0; a.xcd_cols = 0;
     if (splits_out) *splits_out = pl.splits;
     const int bm = bm_for(a.M, a.K);
     dim3 grid((a.N + SK_BN - 1) / SK_BN, 1, pl.splits);
@@ -1015,6 +1025,7 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   a.n_full = pl.n_full;
   a.tail_sp = pl.splits;
   a.n_tail0 = pl.n_tail0;
+  a.xcd_cols = mt <= (pl.kind == GK_BIG ? BIG_GM : TILED_GM) ? pl.n_full / mt / 8 * 8 : 0;
   const long items = (long)pl.n_full + ((long)mt * nt - pl.n_full) * pl.splits;
   if (pl.kind == GK_BIG)
     hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(NT), 0, st, a);
