@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity import Report, assert_report, oracle_decoder, teacher_forced_block
+from parity import Report, assert_report, compare_step, oracle_decoder, teacher_forced_block
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,52 @@ def test_small_bf16_workload_teacher_forced():
         teacher_forced_block(cfg, h, dec, synth.block_state_np(cfg, b), b, rep)
         _log("block", b, rep)
     assert_report(cfg, rep)
+
+
+def test_bf16_split_tail_plans_rows():
+    """1536-row refresh (batch 4 x 384 positions, d 2048, ffn 5632): the q/k/v and gate/up GEMMs
+    run whole columns XCD by XCD and split the remaining columns K-wise, the down projection
+    splits every tile, and the last layer continues with the block rows only.  The refresh
+    statistics are bit-exact under a batch-row permutation (every row of a column is summed in
+    the same order wherever its tile lands), and batch row 0 is teacher-forced against the
+    oracle over one block."""
+    cfg = small_bf16(d_model=2048, n_heads=16, n_kv_heads=16, head_dim=128, ffn_dim=5632,
+                     vocab=4096, mask_id=4095, batch=4, prompt_len=320, gen_length=64,
+                     block_size=32)
+    _log("case split-tail plans, batch 4 x 384")
+    h = _handle(cfg)
+    b = 1
+    x0 = synth.block_state_np(cfg, b)
+    h.set_tokens(x0)
+    h.block_begin(b)
+    a = h.get_step_info()
+    perm = np.random.default_rng(5).permutation(cfg["batch"])
+    h.set_tokens(x0[perm])
+    h.block_begin(b)
+    p = h.get_step_info()
+    for k in ("tok", "conf", "p2"):
+        assert np.array_equal(p[k], a[k][perm]), k
+    ocfg = dict(cfg, batch=1)
+    dec = oracle_decoder(ocfg)
+    rep = Report()
+    dec.set_tokens(x0[:1])
+    h.set_tokens(x0)
+    dec.block_begin(b)
+    h.block_begin(b)
+    for _ in range(cfg["block_size"]):
+        x_before = dec.x.copy()
+        rec, done = dec.step()
+        h.denoise_step()
+        info = {k: v[:1] for k, v in h.get_step_info().items()}
+        lg = h.debug_block_logits()[:1].cpu().numpy()
+        compare_step(ocfg, rec, x_before, info, lg, rep)
+        xg = h.get_tokens()
+        xg[:1] = dec.x
+        h.set_tokens(xg)
+        if done:
+            break
+    _log(rep)
+    assert_report(ocfg, rep)
 
 
 # ------------------------------------------------------------------------------ invariants
