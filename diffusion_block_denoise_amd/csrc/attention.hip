@@ -255,12 +255,15 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 // memory into a ring of 3 LDS slots (global_load_lds, 16 bytes per lane, no register staging),
 // two tiles ahead, one barrier per tile; every wave runs the per-wave kernel's MFMA sequence
 // with its operands read from LDS.  In a slot, row r's 16-byte chunk c sits at chunk position
-// r * CPR + (c ^ f(r)) (CPR chunks per row; f(r) = r & 7 for rows of 8 or more chunks, else
-// (r >> 1) & 3), so the fragment reads of 8 consecutive rows hit distinct banks.  When the
+// r * CPR + (c ^ f(r)) (CPR chunks per row: f(r) = r & 15 for 16, (r >> 1) & 7 for 8,
+// (r >> 2) & 3 for 4), so the fragment reads of 16 consecutive rows cover the 64 banks (256
+// bytes) of the LDS once.  When the
 // workgroups cannot fill the GPU the keys are split into chunks (partials + the merge kernel).
 static constexpr int AW_WAVES = 4, AW_SLOTS = 3;
 
-__device__ inline int aw_swz(int r, int cpr) { return cpr >= 8 ? (r & 7) : ((r >> 1) & 3); }
+__device__ inline int aw_swz(int r, int cpr) {
+  return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
 
 template <int HD>
 __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(

@@ -283,15 +283,26 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int s
 }
 
 // ---------------------------------------------------------------------------------------------
-// Tile t -> (M tile, N tile): groups of GM rows of M tiles, M tile index fastest inside a group.
-// The workgroups resident at one time then share a few A row blocks and a few W panels, so both
-// stay in the caches when A is too large for them (a refresh of many batch rows).  With at most
-// GM rows of M tiles this is plain M-fastest order: a column's tiles are consecutive.
-__device__ inline void tile_coords(int t, int mt, int nt, int gm, int &tm, int &tn) {
+// Tile t -> (M tile, N tile).  The M tiles form groups of GM rows, taken one after another, so
+// the workgroups resident at one time share a few A row blocks (a refresh of many batch rows has
+// far more A than the caches hold).  Inside a group, the first c8 columns (a multiple of 8) are
+// placed XCD by XCD: workgroup t runs on XCD t % 8 and takes the tiles of columns t % 8,
+// t % 8 + 8, ... with the group's M tiles in order, so each W panel is fetched into one XCD's L2;
+// the remaining columns follow one after another, M tile index fastest.  Every group's first
+// tile index is a multiple of 8 (GM is).  With split tiles (a single group) c8 counts only whole
+// columns, so the split columns keep the plain M-fastest order of launch_gemm's plan.
+__device__ inline void tile_coords(int t, int mt, int nt, int gm, int c8, int &tm, int &tn) {
   const int g = t / (gm * nt), r = t - g * gm * nt;
   const int rows = min(gm, mt - g * gm);
-  tm = g * gm + r % rows;
-  tn = r / rows;
+  if (r < c8 * rows) {
+    const int k = r >> 3;
+    tn = (r & 7) + 8 * (k / rows);
+    tm = g * gm + k % rows;
+  } else {
+    const int r2 = r - c8 * rows;
+    tn = c8 + r2 / rows;
+    tm = g * gm + r2 % rows;
+  }
 }
 static constexpr int TILED_GM = 16, BIG_GM = 8;
 
@@ -316,11 +327,7 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
   // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
   // split covers whole columns and every row of a column is summed in the same order) and K range
   const int mt = (a.M + BM - 1) / BM;
-  int w = blockIdx.x;
-  if (w < a.xcd_cols * mt) {  // XCD-aware: the columns of XCD w % 8, M tiles in order
-    const int x = w & 7, k = w >> 3;
-    w = (x + 8 * (k / mt)) * mt + k % mt;
-  }
+  const int w = blockIdx.x;
   int tile = w, split = -1, kbeg = 0, kend = a.K;
   if (w >= a.n_full) {
     const int j = w - a.n_full;
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
     if (a.tail_sp == 1) split = -1;
   }
   int tm, tn;
-  tile_coords(tile, mt, (a.N + BN - 1) / BN, TILED_GM, tm, tn);
+  tile_coords(tile, mt, (a.N + BN - 1) / BN, TILED_GM, a.xcd_cols, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Global -> register staging: 16-byte chunks, 8 per 64-wide row.  Native vector types: arrays
@@ -450,13 +457,13 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 // (A) or 8 (W, hi and lo) MFMAs.  K advances in stages of 32 through a ring of 3 LDS slots
 // filled straight from global memory (global_load_lds, 16 bytes per lane, no register staging),
 // 2 stages ahead; one barrier per stage.  In a slot, a [rows][32] region holds row r's 16-byte
-// chunk c at chunk position 4 r + (c ^ ((r >> 1) & 3)): 8 consecutive rows of one chunk column
-// then cover all 32 banks, so the fragment reads are conflict-free.
+// chunk c at chunk position 4 r + (c ^ ((r >> 2) & 3)): 16 consecutive rows of one chunk column
+// then cover all 64 banks of the LDS (256 bytes), so the fragment reads are conflict-free.
 static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NS = 3;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ inline int bg_pos(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+__device__ inline int bg_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   constexpr int REG = BG_BM * BG_BK * 2;     // one [256][32] bf16 region: 16 KB
@@ -470,11 +477,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   // work item -> tile and K range, as in gemm_mfma_kernel
   const int mt = (a.M + BG_BM - 1) / BG_BM;
-  int w = blockIdx.x;
-  if (w < a.xcd_cols * mt) {  // XCD-aware: the columns of XCD w % 8, M tiles in order
-    const int x = w & 7, k = w >> 3;
-    w = (x + 8 * (k / mt)) * mt + k % mt;
-  }
+  const int w = blockIdx.x;
   int tile = w, split = -1, kbeg = 0, kend = a.K;
   if (w >= a.n_full) {
     const int j = w - a.n_full;
@@ -485,19 +488,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
     if (a.tail_sp == 1) split = -1;
   }
   int tm, tn;
-  tile_coords(tile, mt, (a.N + BG_BN - 1) / BG_BN, BIG_GM, tm, tn);
+  tile_coords(tile, mt, (a.N + BG_BN - 1) / BG_BN, BIG_GM, a.xcd_cols, tm, tn);
   const int m0 = tm * BG_BM, n0 = tn * BG_BN;
   const int T = (kend - kbeg) / BG_BK;
 
   // Loads: wave w's instruction j (0..3) of each region fills chunk positions (4 w + j) * 64 +
-  // lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 1) & 3).  Rows past M read
+  // lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 2) & 3).  Rows past M read
   // row M - 1 and panels past the last one read the last one (their outputs are never written).
   const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
   size_t aoff[4];
   const uint16_t *wsrc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int pos = (wave * 4 + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 1) & 3);
+    const int pos = (wave * 4 + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
     aoff[j] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda + c * 8;
     wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
   }
@@ -525,7 +528,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // fragment rows: lane l reads row (l & 31) of each 32-row block, chunk kk * 2 + (l >> 5)
-  const int frow = lane & 31, fsw = (frow >> 1) & 3, fhalf = lane >> 5;
+  const int frow = lane & 31, fsw = (frow >> 2) & 3, fhalf = lane >> 5;
   const int arow = (wm * 128 + frow) * 64, wrow = (wn * 128 + frow) * 64;
   // Fragments are double-buffered per 16-wide k step: the reads of the next step go out before
   // the MFMAs of the current one.
@@ -1025,7 +1028,8 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   a.n_full = pl.n_full;
   a.tail_sp = pl.splits;
   a.n_tail0 = pl.n_tail0;
-  a.xcd_cols = mt <= (pl.kind == GK_BIG ? BIG_GM : TILED_GM) ? pl.n_full / mt / 8 * 8 : 0;
+  // columns placed XCD by XCD: the whole-tile columns (all of them without splits)
+  a.xcd_cols = (mt <= (pl.kind == GK_BIG ? BIG_GM : TILED_GM) ? pl.n_full / mt : nt) / 8 * 8;
   const long items = (long)pl.n_full + ((long)mt * nt - pl.n_full) * pl.splits;
   if (pl.kind == GK_BIG)
     hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(NT), 0, st, a);

@@ -90,9 +90,9 @@ struct GemmArgs {
   // epilogue; each later tile (all of them columns from n_tail0 on) is split tail_sp ways.
   float *partial;
   int n_full, tail_sp, n_tail0;
-  // tiled kernels: the first xcd_cols * (M tiles) workgroups (xcd_cols a multiple of 8) take the
-  // whole tiles of those columns XCD by XCD (workgroup b runs on XCD b % 8): XCD x gets columns
-  // x, x + 8, ..., each with all its M tiles, so a W panel is fetched into one L2 only
+  // tiled kernels: in each group of M tiles, the tiles of the first xcd_cols columns (a multiple
+  // of 8) are placed XCD by XCD (workgroup b runs on XCD b % 8): XCD x gets columns x, x + 8,
+  // ..., each with the group's M tiles, so a W panel is fetched into one L2 only
   int xcd_cols;
   int epi;
   // epilogue operands
