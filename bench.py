@@ -106,6 +106,36 @@ def roofline(prof, dtype):
             "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
 
 
+def phase_roofline(cfg, refresh_ms, step_ms):
+    """Roofline time of a refresh and of a cached step from their algorithmic work, against the
+    measured medians, for the dual-cache full-context decode (the rows and context of the other
+    modes vary by block; null there).  Work counted once: every weight (bf16) per forward, every
+    cached K/V element (a 4-byte hi/lo pair) read once per (batch row, K/V head, layer), 2 flops
+    per multiply-add of the projections, the lm_head over the block rows and the attention."""
+    if cfg["use_cache"] != 2 or cfg["suffix_window"] >= 0 or cfg["attention"] != "full":
+        return None
+    B, L, Bs = cfg["batch"], cfg["prompt_len"] + cfg["gen_length"], cfg["block_size"]
+    d, H, Hkv, hd, F, V, nl = (cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+                               cfg["ffn_dim"], cfg["vocab"], cfg["n_layers"])
+    wsz = 2 if cfg["dtype"] == "bf16" else 4
+    layer_params = d * (H + 2 * Hkv) * hd + H * hd * d + 3 * d * F
+    wbytes = (nl * layer_params + V * d) * wsz
+    kv = 2.0 * B * Hkv * L * hd * 4 * nl
+    peak_f = (BF16_PEAK_TFLOPS if cfg["dtype"] == "bf16" else F32_PEAK_TFLOPS) * 1e12
+    out = {}
+    for name, M, keys_read, ms in (("refresh", B * L, 0.0, refresh_ms),
+                                   ("cached_step", B * Bs, kv, step_ms)):
+        flops = 2.0 * M * nl * layer_params + 2.0 * B * Bs * V * d + 4.0 * M * L * H * hd * nl
+        kv_written = 2.0 * M * Hkv * hd * 4 * nl
+        byts = wbytes + keys_read + kv_written
+        t_hbm, t_mfma = byts / (HBM_PEAK_GBS * 1e9), flops / peak_f
+        roof = max(t_hbm, t_mfma) * 1e3
+        out[name] = {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "roofline_ms": roof,
+                     "measured_ms": ms, "frac": roof / ms if ms else None,
+                     "bytes": byts, "flops": flops}
+    return out
+
+
 def cpu_baseline(cfg, W, n_full, n_cached, tokens, sample_layers=2):
     """The oracle on a bounded sample: `sample_layers` of the model's layers, one refresh forward
     over block 1's context and one dual-cache step over its block rows in batch row 0, plus the
@@ -269,9 +299,15 @@ def main():
         "refreshes_per_generate": st["full_forwards"],
         "cached_steps_per_generate": st["cached_forwards"],
         "refresh_latency_ms": refresh_ms, "cached_step_latency_ms": step_ms,
+        "phase_roofline": phase_roofline(cfg, refresh_ms, step_ms),
         "kernel_classes": {k: {"launches": v["launches"], "ms": v["ms"],
                                "GB_per_s": v["bytes"] / (v["ms"] / 1e3) / 1e9 if v["ms"] else None,
-                               "TFLOP_per_s": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["ms"] else None}
+                               "TFLOP_per_s": v["flops"] / (v["ms"] / 1e3) / 1e12 if v["ms"] else None,
+                               "hbm_frac": v["bytes"] / (v["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS
+                               if v["ms"] else None,
+                               "mfma_frac": v["flops"] / (v["ms"] / 1e3) / 1e12 / (
+                                   BF16_PEAK_TFLOPS if cfg["dtype"] == "bf16" else F32_PEAK_TFLOPS)
+                               if v["ms"] else None}
                            for k, v in prof.items()},
         "cpu_baseline": None,
     }
