@@ -451,31 +451,43 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Large-tile bf16 MFMA kernel for many rows (block refresh of long contexts and batches).  A
-// workgroup of 4 waves owns a 256 x 256 tile; each wave a 128 x 128 quadrant as 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (256 accumulator registers), so every fragment read from LDS feeds 4
-// (A) or 8 (W, hi and lo) MFMAs.  K advances in stages of 32 through a ring of 3 LDS slots
-// filled straight from global memory (global_load_lds, 16 bytes per lane, no register staging),
-// 2 stages ahead; one barrier per stage.  In a slot, a [rows][32] region holds row r's 16-byte
-// chunk c at chunk position 4 r + (c ^ ((r >> 2) & 3)): 16 consecutive rows of one chunk column
-// then cover all 64 banks of the LDS (256 bytes), so the fragment reads are conflict-free.
+// Large-tile bf16 MFMA kernel for many rows (block refresh of long contexts and batches, and the
+// widest projections).  A workgroup of 8 waves (2 x 4, two per SIMD) owns a 256 x 256 tile; each
+// wave a 128 x 64 piece as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, so a W fragment read from
+// LDS feeds 8 MFMAs (4 blocks, hi and lo) and an A fragment 2.  K advances in stages of 32 through
+// a ring of 3 LDS slots filled straight from global memory (global_load_lds, 16 bytes per lane,
+// no register staging), 2 stages ahead; one barrier per stage; the fragment reads of the next
+// 16-wide step go out before the MFMAs of the current one.  In a slot, a [rows][32] region holds
+// row r's 16-byte chunk c at chunk position 4 r + (c ^ ((r >> 2) & 3)): 16 consecutive rows of
+// one chunk column then cover all 64 banks of the LDS (256 bytes), so the fragment reads are
+// conflict-free.  (Measured against a 4-wave version with 128 x 128 per wave: ~5 % faster, the
+// second wave per SIMD covers the barrier and fragment-read gaps.)
 static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NS = 3;
+static constexpr int BG_WGM = 2, BG_WGN = 4, BG_NT = 64 * BG_WGM * BG_WGN;  // waves, threads
+static constexpr int BG_WM = BG_BM / BG_WGM / 32, BG_WN = BG_BN / BG_WGN / 32;  // blocks per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ inline int bg_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+// s_waitcnt immediate: vmcnt vm (6 bits), lgkmcnt lgkm (4 bits), expcnt not waited on
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
 
-__global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
   constexpr int REG = BG_BM * BG_BK * 2;     // one [256][32] bf16 region: 16 KB
   constexpr int STAGE = 3 * REG;             // A hi, A lo, W
-  constexpr int LDC = 2 * 128 + 4;           // epilogue: 128 rows x 256 columns of fp32
+  constexpr int IR = BG_BM * 4 / BG_NT;      // global_load_lds per wave and region: 2
+  constexpr int VM_STAGE = 3 * IR;           // ... and per stage
+  constexpr int LDC = 128 + 4;               // epilogue: 128 x 128 pieces of fp32
   static_assert(128 * LDC * 4 <= BG_NS * STAGE, "epilogue tile must fit the ring");
+  static_assert(BG_BM == BG_BN && IR * BG_NT == BG_BM * 4, "one chunk per lane and load");
   __shared__ __align__(1024) unsigned char smem[BG_NS * STAGE];
   float *Ct = (float *)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // work item -> tile and K range, as in gemm_mfma_kernel
+  const int wm = wave / BG_WGN, wn = wave % BG_WGN;
+  // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
+  // split covers whole columns and every row of a column is summed in the same order) and K range
   const int mt = (a.M + BG_BM - 1) / BG_BM;
   const int w = blockIdx.x;
   int tile = w, split = -1, kbeg = 0, kend = a.K;
@@ -492,15 +504,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   const int m0 = tm * BG_BM, n0 = tn * BG_BN;
   const int T = (kend - kbeg) / BG_BK;
 
-  // Loads: wave w's instruction j (0..3) of each region fills chunk positions (4 w + j) * 64 +
-  // lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 2) & 3).  Rows past M read
-  // row M - 1 and panels past the last one read the last one (their outputs are never written).
+  // Loads: wave w's instruction j (0..IR-1) of each region fills chunk positions
+  // (IR w + j) * 64 + lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 2) & 3).  Rows
+  // past M read row M - 1 and panels past the last one read the last one (their outputs are
+  // never written).
   const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
-  size_t aoff[4];
-  const uint16_t *wsrc[4];
+  size_t aoff[IR];
+  const uint16_t *wsrc[IR];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pos = (wave * 4 + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
+  for (int j = 0; j < IR; ++j) {
+    const int pos = (wave * IR + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
     aoff[j] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda + c * 8;
     wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
   }
@@ -509,50 +522,51 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   // iteration has the same number of loads in flight
   auto issue = [&](int t) {
     const int k0 = kbeg + min(t, T - 1) * BG_BK;
-    unsigned char *st = smem + (t % BG_NS) * STAGE + wave * 4096;
+    unsigned char *st = smem + (t % BG_NS) * STAGE + wave * (IR * 1024);
     const size_t kw = (size_t)(k0 / PW_K) * (PW_ROWS * PW_K);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < IR; ++j) {
       __builtin_amdgcn_global_load_lds((const void *)(ahi + aoff[j] + k0), (lds_void *)(st + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(alo + aoff[j] + k0), (lds_void *)(st + REG + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(wsrc[j] + kw), (lds_void *)(st + 2 * REG + j * 1024), 16, 0, 0);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[BG_WM][BG_WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BG_WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < BG_WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // fragment rows: lane l reads row (l & 31) of each 32-row block, chunk kk * 2 + (l >> 5)
   const int frow = lane & 31, fsw = (frow >> 2) & 3, fhalf = lane >> 5;
-  const int arow = (wm * 128 + frow) * 64, wrow = (wn * 128 + frow) * 64;
+  const int arow = (wm * (BG_BM / BG_WGM) + frow) * 64, wrow = (wn * (BG_BN / BG_WGN) + frow) * 64;
   // Fragments are double-buffered per 16-wide k step: the reads of the next step go out before
   // the MFMAs of the current one.
-  bf16x8_t fh[2][4], fl[2][4], fb[2][4];
+  bf16x8_t fh[2][BG_WM], fl[2][BG_WM], fb[2][BG_WN];
   auto read_frags = [&](int t, int kk, int buf) {
     const unsigned char *st = smem + (t % BG_NS) * STAGE;
     const int cb = ((kk * 2 + fhalf) ^ fsw) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BG_WM; ++i) {
       fh[buf][i] = *(const bf16x8_t *)(st + arow + i * 2048 + cb);
       fl[buf][i] = *(const bf16x8_t *)(st + REG + arow + i * 2048 + cb);
-      fb[buf][i] = *(const bf16x8_t *)(st + 2 * REG + wrow + i * 2048 + cb);
     }
+#pragma unroll
+    for (int j = 0; j < BG_WN; ++j) fb[buf][j] = *(const bf16x8_t *)(st + 2 * REG + wrow + j * 2048 + cb);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BG_WM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < BG_WN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BG_WM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < BG_WN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
   };
   auto barrier = [&]() {
@@ -567,19 +581,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
   issue(0);
   issue(1);
   issue(2);
-  __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24): stage 0 has landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * VM_STAGE, 15));  // stage 0 has landed
   barrier();
   read_frags(0, 0, 0);
   for (int t = 0; t < T; ++t) {
-    // at most 12 reads outstanding at a time (the LDS counter only counts to 15)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): buffer 0 is in registers
+    // 2 BG_WM + BG_WN = 10 reads in flight at most (the LDS counter only counts to 15)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // buffer 0 is in registers
     read_frags(t, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    // stage t + 1 has landed once only stage t + 2's 12 loads are outstanding; all of this
+    // stage t + 1 has landed once only stage t + 2's loads are outstanding; all of this
     // wave's reads of stage t are complete before the barrier
-    __builtin_amdgcn_s_waitcnt(0x007C);  // vmcnt(12) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM_STAGE, 0));
     barrier();
     issue(t + 3);  // into the slot of stage t
     read_frags(min(t + 1, T - 1), 0, 0);
@@ -587,33 +601,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_big_kernel(const GemmArgs a) {
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes the ring
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no load still writes the ring
   __syncthreads();
-  // Epilogue in two row halves: the waves of half h write their 128 x 128 quadrants into a
-  // 128 x 256 C tile, then all threads run the 128 x 128 epilogue on each column half.
+  // Epilogue in 128 x 128 pieces: the waves whose 128 x 64 pieces lie in piece (h, q) write them
+  // into the C tile, then the first 256 threads run the epilogue on it.
+  constexpr int QR = BG_BM / BG_WGM, QC = BG_BN / BG_WGN;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
+  for (int h = 0; h < BG_BM / 128; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < BG_BN / 128; ++q) {
+      const int r0 = wm * QR - h * 128, c0 = wn * QC - q * 128;
+      if (r0 >= 0 && r0 < 128 && c0 >= 0 && c0 < 128) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < BG_WM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
-            Ct[row * LDC + wn * 128 + j * 32 + frow] = acc[i][j][r];
-          }
+          for (int j = 0; j < BG_WN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = r0 + i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
+              Ct[row * LDC + c0 + j * 32 + frow] = acc[i][j][r];
+            }
+      }
+      __syncthreads();
+      if (tid < NT) {
+        if (split >= 0)
+          write_partial<128, 128>(a, split, Ct, LDC, m0 + h * 128, n0 + q * 128);
+        else
+          run_epilogue<bf16, 128, 128>(a, Ct, LDC, m0 + h * 128, n0 + q * 128);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (split >= 0)
-        write_partial<128, 128>(a, split, Ct + q * 128, LDC, m0 + h * 128, n0 + q * 128);
-      else
-        run_epilogue<bf16, 128, 128>(a, Ct + q * 128, LDC, m0 + h * 128, n0 + q * 128);
-    }
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -807,8 +824,8 @@ static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16)
 //   reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted on MI355X to the 8B-shape
 //   projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K step of 64 alone on its
 //   CU and 1.98 us when two share it (they are limited by the CU, not by latency); a 256 x 256
-//   workgroup (one per CU) 4.0 us.  The large-tile kernel serves M >= 2048 when its tiles fill at
-//   least one round.
+//   workgroup (one per CU) 3.7 us.  The large-tile kernel serves M >= 512 when its tiles fill at
+//   least one round (at 768 rows: the gate/up projection, ~4 % faster than 128 x 128 tiles).
 enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3 };
 
 struct SplitPlan {
@@ -883,7 +900,7 @@ static double cu_makespan(long n_full, int it_full, long n_tail, int it_tail, in
 static SplitPlan tile_plan(int kind, int M, int N, int K) {
   const bool big = kind == GK_BIG;
   const int bm = big ? 256 : 128, bn = big ? 256 : 128, per_cu = big ? 1 : 2;
-  const double t1 = big ? 4.0 : 1.25, t2 = 1.98;
+  const double t1 = big ? 3.7 : 1.25, t2 = 1.98;
   const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn, iters = K / 64;
   const long tiles = (long)mt * nt;
   SplitPlan best_plan{kind, 1, K, (int)tiles, N};
@@ -919,7 +936,7 @@ static int choose_kind(int M, int N, int K, int dtype) {
   if (dtype == 0) return GK_F32;
   if (use_skinny(M, K)) return GK_SKINNY;
   const long big_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
-  if (M >= 2048 && big_tiles >= 256 && K % 64 == 0) return GK_BIG;
+  if (M >= 512 && big_tiles >= 256 && K % 64 == 0) return GK_BIG;
   return GK_TILED;
 }
 
@@ -1032,7 +1049,7 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   a.xcd_cols = (mt <= (pl.kind == GK_BIG ? BIG_GM : TILED_GM) ? pl.n_full / mt : nt) / 8 * 8;
   const long items = (long)pl.n_full + ((long)mt * nt - pl.n_full) * pl.splits;
   if (pl.kind == GK_BIG)
-    hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(BG_NT), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), dim3((unsigned)items), dim3(NT), 0, st, a);
   if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
