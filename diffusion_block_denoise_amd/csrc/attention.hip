@@ -87,7 +87,10 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   constexpr int DB = HD / 32;  // 32-dim blocks of the output
   const int G = H / Hkv;
   const int nrows = rs.nR * G;
-  const int qt = blockIdx.x, bg = blockIdx.y, split = blockIdx.z;
+  // grid (batch row x K/V head, query tile, key chunk): the query tiles of one (batch row, K/V
+  // head) are gridDim.x workgroups apart; with B * Hkv a multiple of 8 they run on one XCD
+  // (workgroup i on XCD i % 8), where the second reader of a K/V tile finds it in the L2
+  const int bg = blockIdx.x, qt = blockIdx.y, split = blockIdx.z;
   const int b = bg / Hkv, g = bg % Hkv;
   const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
 
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
       }
   } else {
     // part[split][bg][qt][col][HD + 2]
-    float *pp = part + ((((size_t)split * gridDim.y + bg) * gridDim.x + qt) * 32 + col) * (HD + 2);
+    float *pp = part + ((((size_t)split * gridDim.x + bg) * gridDim.y + qt) * 32 + col) * (HD + 2);
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -596,7 +599,7 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
   }
   int splits, chunk;
   attn_plan(rs, H, Hkv, splits, chunk);
-  dim3 grid(nqt, rs.B * Hkv, splits);
+  dim3 grid(rs.B * Hkv, nqt, splits);
 #define ATTN_CASE(HDV)                                                                          \
   case HDV:                                                                                     \
     hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \
