@@ -78,6 +78,33 @@ size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
   return (size_t)splits * rs.B * Hkv * nqt * 32 * (hd + 2) * sizeof(float);
 }
 
+// Workgroup order of the attention grids (x = blocks of 8 (batch row, K/V head) pairs, each
+// block holding the query tiles (or tile groups) of its pairs 8 apart; y = 1; z = key chunk):
+// workgroup i runs on XCD i % 8, so the tiles of one pair run on one XCD, where the second
+// reader of a K/V tile finds it in the L2, and the workgroups in flight at one time cover few
+// pairs.  Pairs past B * Hkv (the last block's padding) return at once.
+__device__ inline void attn_grid_order(int x, int npairs, int &pair, int &tile) {
+  const int ntiles = gridDim.x / ((npairs + 7) / 8 * 8);
+  const int blk = x / (8 * ntiles), r = x - blk * 8 * ntiles;
+  tile = r >> 3;
+  pair = blk * 8 + (r & 7);
+}
+static inline unsigned attn_grid_x(int npairs, int ntiles) {
+  return (unsigned)((npairs + 7) / 8 * 8 * ntiles);
+}
+
+// Reference maximum of the online softmax (log2 units).  The probabilities of a tile are
+// exp2(s - m) against a per-query reference m that moves only when a score exceeds it by more
+// than REF_SLACK: then m becomes the running maximum and the output and sum so far are rescaled.
+// Otherwise p may reach 2^REF_SLACK, far from fp32 and bf16 limits, and since the output and
+// the sum share the reference the normalised result is the same as with the exact running
+// maximum (up to rounding).  With the exact maximum nearly every tile moved some query's
+// maximum in a 32-query tile, so the (register-file) rescale of the output ran every tile.
+static constexpr float REF_SLACK = 8.0f;
+__device__ inline float ref_max(float mref, float tmax) {
+  return tmax > mref + REF_SLACK ? tmax : mref;  // mref = -inf: any visible score sets it
+}
+
 template <int HD>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
@@ -87,10 +114,11 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   constexpr int DB = HD / 32;  // 32-dim blocks of the output
   const int G = H / Hkv;
   const int nrows = rs.nR * G;
-  // grid (batch row x K/V head, query tile, key chunk): the query tiles of one (batch row, K/V
-  // head) are gridDim.x workgroups apart; with B * Hkv a multiple of 8 they run on one XCD
-  // (workgroup i on XCD i % 8), where the second reader of a K/V tile finds it in the L2
-  const int bg = blockIdx.x, qt = blockIdx.y, split = blockIdx.z;
+  const int npairs = rs.B * Hkv, split = blockIdx.z;
+  int bg, qt;
+  attn_grid_order(blockIdx.x, npairs, bg, qt);
+  if (bg >= npairs) return;
+  const int nqt = gridDim.x / ((npairs + 7) / 8 * 8);
   const int b = bg / Hkv, g = bg % Hkv;
   const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
 
@@ -175,7 +203,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
       tmax = fmaxf(tmax, s[i]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrun, tmax);
+    const float mnew = ref_max(mrun, tmax);
     const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
     // P^T as hi/lo B operands of the next product; register i of k-step i/8 holds key slot i%8.
     // (A lane with no visible key yet has mnew = -inf: its probabilities are 0, not NaN.)
@@ -192,22 +220,23 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
     psum += __shfl_xor(psum, 32, 64);
     lsum = lsum * alpha + psum;
     mrun = mnew;
-    // rescale the running output only when some lane's maximum moved (alpha is exactly 1
-    // otherwise, so skipping changes nothing); after the first tiles it rarely moves
+    // rescale the running output only when some lane's reference moved (alpha is exactly 1
+    // otherwise, so skipping changes nothing); after the first tile it rarely moves
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
     }
+    // consecutive MFMAs update different accumulators (the DB chains run side by side)
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vl[d][ks], ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], pl[ks], o[d], 0, 0, 0);
-      }
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], ph[ks], o[d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vl[d][ks], ph[ks], o[d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.vh[d][ks], pl[ks], o[d], 0, 0, 0);
     }
   };
   // Unrolled by two so that the two tile buffers stay in fixed registers.  Past the chunk's end
@@ -241,7 +270,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
       }
   } else {
     // part[split][bg][qt][col][HD + 2]
-    float *pp = part + ((((size_t)split * gridDim.x + bg) * gridDim.y + qt) * 32 + col) * (HD + 2);
+    float *pp = part + ((((size_t)split * npairs + bg) * nqt + qt) * 32 + col) * (HD + 2);
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -262,7 +291,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 // (r >> 2) & 3 for 4), so the fragment reads of 16 consecutive rows cover the 64 banks (256
 // bytes) of the LDS once.  When the
 // workgroups cannot fill the GPU the keys are split into chunks (partials + the merge kernel).
-static constexpr int AW_WAVES = 4, AW_SLOTS = 3;
+static constexpr int AW_WAVES = 4, AW_SLOTS = 4;
 
 __device__ inline int aw_swz(int r, int cpr) {
   return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
@@ -284,10 +313,14 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
 
   const int G = H / Hkv;
   const int nrows = rs.nR * G;
-  const int bg = blockIdx.y, split = blockIdx.z;
+  const int npairs = rs.B * Hkv, split = blockIdx.z;
+  int bg, grp;
+  attn_grid_order(blockIdx.x, npairs, bg, grp);
+  if (bg >= npairs) return;  // the whole workgroup, before any barrier
+  const int n_qt = gridDim.x / ((npairs + 7) / 8 * 8) * AW_WAVES;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int qt = blockIdx.x * AW_WAVES + wave;
+  const int qt = grp * AW_WAVES + wave;
   const int r = qt * 32 + col;
   const bool valid = r < nrows;
   const int pi = valid ? r / G : 0;
@@ -341,22 +374,9 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   // fragment positions (bytes in a plane): K row col, chunk 2 kk + half; V^T row d * 32 + col,
   // chunk 2 ks + half
   const int ksw = aw_swz(col, KCPR), krow = col * KCPR;
-  issue(0);
-  issue(1);
-  for (int u = 0; u < T; ++u) {
-    // tile u has landed once only tile u + 1's loads are outstanding (vmcnt(LPW))
-    if constexpr (LPW == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-    else if constexpr (LPW == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-    else __builtin_amdgcn_s_waitcnt(0x0F72);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave's part of tile u is in LDS; tile u - 1 is done
-    asm volatile("" ::: "memory");
-    issue(u + 2);                  // into the slot of tile u - 1
+  // S^T of one tile from its slot (all K fragments read before the first MFMA)
+  auto scores = [&](int u) {
     const unsigned char *cur = lds + (u % AW_SLOTS) * SLOT;
-    const int kb = (t0 + u) * 32;
-    // all K fragments of the tile are read before the first MFMA, and all V^T fragments before
-    // the softmax, so each LDS latency is paid once per tile (the scheduler would otherwise wait
-    // on every pair of reads)
     bf16x8_t kh[KS], kl[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -364,7 +384,6 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
       kh[kk] = *(const bf16x8_t *)(cur + pos);
       kl[kk] = *(const bf16x8_t *)(cur + PLANE + pos);
     }
-    __builtin_amdgcn_sched_barrier(0);
     f32x16 sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = 0.f;
@@ -374,6 +393,92 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], sc, 0, 0, 0);
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], sc, 0, 0, 0);
     }
+    return sc;
+  };
+  // tile u has landed once only tile u + 1's loads are outstanding (vmcnt(LPW)); the barrier
+  // also tells that every wave is done with the slot the next issue overwrites
+  auto land_and_sync = [&]() {
+    if constexpr (LPW == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if constexpr (LPW == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else __builtin_amdgcn_s_waitcnt(0x0F72);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Software pipeline over the key tiles: the MFMAs of tile u + 1's scores are issued next to
+  // the softmax of tile u, so the matrix cores work while the wave's VALU computes the
+  // probabilities (one wave per SIMD: the softmax alone would leave the MFMA pipe idle).  Ring
+  // of 4 slots: at iteration u tiles u and u + 1 are resident, u + 2 is landing and u + 3 goes
+  // into the slot of tile u - 1, which every wave finished before this iteration's barrier; so
+  // tile u's V^T fragments can be read after the softmax (K and V^T fragments are never live
+  // together).
+  issue(0);
+  issue(1);
+  land_and_sync();  // tile 0
+  issue(2);
+  f32x16 sc = scores(0);
+  for (int u = 0; u < T; ++u) {
+    const int kb = (t0 + u) * 32;
+    // (the last iteration repeats the clamped tile's scores, unused, to keep the block straight)
+    land_and_sync();  // tile u + 1
+    issue(u + 3);     // into the slot of tile u - 1
+    __builtin_amdgcn_sched_barrier(0);
+    // K fragments of tile u + 1 (all read before the first MFMA)
+    const unsigned char *nxt = lds + (min(u + 1, T - 1) % AW_SLOTS) * SLOT;
+    bf16x8_t kh[KS], kl[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int pos = (krow + ((kk * 2 + half) ^ ksw)) * 16;
+      kh[kk] = *(const bf16x8_t *)(nxt + pos);
+      kl[kk] = *(const bf16x8_t *)(nxt + PLANE + pos);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The score MFMAs of tile u + 1 (a dependent chain of 3 KS) interleaved with the softmax of
+    // tile u, one softmax step after each MFMA: the steps are independent of the chain, so the
+    // VALU works while the matrix core does.
+    f32x16 sn, sn1, sn2;  // three independent chains (hi K, lo K, lo q), summed at the end
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sn[i] = sn1[i] = sn2[i] = 0.f;
+    float tmax = -INFINITY, mnew = 0.f, alpha = 0.f, psum = 0.f;
+    bf16x8_t ph[2], pl[2];
+    auto step = [&](int k) {  // k: 0..15 mask and max; 16 row max; 17..32 exp; 33 sums
+      if (k < 16) {
+        const int key = kb + 8 * (k >> 2) + 4 * half + (k & 3);
+        sc[k] = key < klim ? sc[k] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, sc[k]);
+      } else if (k == 16) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        mnew = ref_max(mrun, tmax);
+        alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+      } else if (k < 33) {
+        const int i = k - 17;
+        const float pv = mnew == -INFINITY ? 0.f : exp2f(sc[i] - mnew);
+        const __bf16 hi = (__bf16)pv;
+        ph[i >> 3][i & 7] = hi;
+        pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
+        psum += pv;
+      } else {
+        psum += __shfl_xor(psum, 32, 64);
+        lsum = lsum * alpha + psum;
+        mrun = mnew;
+      }
+    };
+#pragma unroll
+    for (int g = 0; g < 3 * KS; ++g) {
+      const int kk = g / 3, term = g % 3;
+      if (term == 0) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], qh[kk], sn, 0, 0, 0);
+      else if (term == 1) sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], sn1, 0, 0, 0);
+      else sn2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], sn2, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      step(g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int g = 3 * KS; g < 34; ++g) step(g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sn[i] = sn[i] + (sn1[i] + sn2[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char *cur = lds + (u % AW_SLOTS) * SLOT;
     bf16x8_t vfh[DB][2], vfl[DB][2];
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
@@ -385,47 +490,25 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
         vfl[d][ks] = *(const bf16x8_t *)(cur + 3 * PLANE + pos);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
-      sc[i] = key < klim ? sc[i] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sc[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrun, tmax);
-    const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
-    bf16x8_t ph[2], pl[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = mnew == -INFINITY ? 0.f : exp2f(sc[i] - mnew);
-      const __bf16 hi = (__bf16)pv;
-      ph[i >> 3][i & 7] = hi;
-      pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
-      psum += pv;
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    lsum = lsum * alpha + psum;
-    mrun = mnew;
-    // rescale the running output only when some lane's maximum moved (alpha is exactly 1
-    // otherwise, so skipping changes nothing); after the first tiles it rarely moves
+    // rescale the running output only when some lane's reference moved (alpha is exactly 1
+    // otherwise, so skipping changes nothing); after the first tile it rarely moves
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
     }
+    // consecutive MFMAs update different accumulators (the DB chains run side by side)
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfl[d][ks], ph[ks], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], pl[ks], o[d], 0, 0, 0);
-      }
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], ph[ks], o[d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfl[d][ks], ph[ks], o[d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], pl[ks], o[d], 0, 0, 0);
     }
+    sc = sn;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
   if (!valid) return;
@@ -445,8 +528,7 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
       }
   } else {
     // part[split][bg][qt][col][HD + 2], as the few-query kernel writes it
-    const int n_qt = gridDim.x * AW_WAVES;
-    float *pp = part + ((((size_t)split * gridDim.y + bg) * n_qt + qt) * 32 + col) * (HD + 2);
+    float *pp = part + ((((size_t)split * npairs + bg) * n_qt + qt) * 32 + col) * (HD + 2);
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -575,7 +657,7 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
     int wsplits, wchunk;
     attn_wide_plan(rs, H, Hkv, wsplits, wchunk);
     const int groups = (nqt + AW_WAVES - 1) / AW_WAVES;
-    dim3 wgrid(groups, rs.B * Hkv, wsplits);
+    dim3 wgrid(attn_grid_x(rs.B * Hkv, groups), 1, wsplits);
 #define ATTNW_CASE(HDV)                                                                          \
   case HDV:                                                                                      \
     hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES), 0, st, (const bf16 *)q, \
@@ -599,7 +681,7 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
   }
   int splits, chunk;
   attn_plan(rs, H, Hkv, splits, chunk);
-  dim3 grid(rs.B * Hkv, nqt, splits);
+  dim3 grid(attn_grid_x(rs.B * Hkv, nqt), 1, splits);
 #define ATTN_CASE(HDV)                                                                          \
   case HDV:                                                                                     \
     hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \
