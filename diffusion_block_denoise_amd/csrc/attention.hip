@@ -541,12 +541,16 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
 }
 
 // Combine the key chunks: one wave per query row slot, lanes over dims.
+static constexpr int MG_ROWS = 4;  // query rows (waves) per merge workgroup
+
 template <int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict__ part, RowSet rs,
-                                                        int H, int Hkv, int n_qt, int splits,
-                                                        bf16 *o_hi, bf16 *o_lo) {
+__global__ __launch_bounds__(64 * MG_ROWS) void attn_merge_kernel(const float *__restrict__ part,
+                                                                  RowSet rs, int H, int Hkv,
+                                                                  int n_qt, int splits,
+                                                                  bf16 *o_hi, bf16 *o_lo) {
   const int G = H / Hkv;
-  const int slot = blockIdx.x;  // (bg, qt, col)
+  const int slot = blockIdx.x * MG_ROWS + (threadIdx.x >> 6);  // (bg, qt, col)
+  if (slot >= rs.B * Hkv * n_qt * 32) return;
   const int col = slot % 32, qt = (slot / 32) % n_qt, bg = slot / 32 / n_qt;
   const int r = qt * 32 + col;
   if (r >= rs.nR * G) return;
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float *__restrict_
   // lane s holds chunk s's running max and sum; every load of the merge is issued before the
   // first one is used (one memory latency instead of one per chunk), and the sums still run in
   // chunk order
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   float m_own = -INFINITY, l_own = 0.f;
   if (lane < splits) {
     m_own = p0[lane * stride + HD];
@@ -665,9 +669,10 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
                        (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, wchunk,    \
                        scale_log2, o_hi, o_lo, part);                                            \
     if (wsplits > 1)                                                                             \
-      hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3(rs.B * Hkv * groups * AW_WAVES * 32),      \
-                         dim3(64), 0, st, (const float *)part, rs, H, Hkv, groups * AW_WAVES,    \
-                         wsplits, o_hi, o_lo);                                                   \
+      hipLaunchKernelGGL(attn_merge_kernel<HDV>,                                                 \
+                         dim3((rs.B * Hkv * groups * AW_WAVES * 32 + MG_ROWS - 1) / MG_ROWS),    \
+                         dim3(64 * MG_ROWS), 0, st, (const float *)part, rs, H, Hkv,             \
+                         groups * AW_WAVES, wsplits, o_hi, o_lo);                                \
     break;
     switch (hd) {
       ATTNW_CASE(32)
@@ -689,8 +694,9 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
                        (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, chunk,    \
                        scale_log2, o_hi, o_lo, part);                                           \
     if (splits > 1)                                                                             \
-      hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3(rs.B * Hkv * nqt * 32), dim3(64), 0, st,  \
-                         (const float *)part, rs, H, Hkv, nqt, splits, o_hi, o_lo);             \
+      hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3((rs.B * Hkv * nqt * 32 + MG_ROWS - 1) / MG_ROWS), \
+                         dim3(64 * MG_ROWS), 0, st, (const float *)part, rs, H, Hkv, nqt, splits, \
+                         o_hi, o_lo);                                                           \
     break;
   switch (hd) {
     ATTN_CASE(32)

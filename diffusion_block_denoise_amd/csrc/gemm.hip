@@ -155,16 +155,17 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
       const int hd = a.head_dim, half = hd / 2, H = a.n_heads, Hkv = a.n_kv_heads;
       const int nq = H * hd, nk = Hkv * hd;
       const RowSet rs = a.rows;
-      for (int e = tid; e < BM * BN; e += NT) {
-        const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
-        if (m >= M || n >= a.N) continue;
-        const int b = m / rs.nR, p = rs.start + m % rs.nR;
-        const int i = n % hd;
-        const float x = Ct[r * ldc + c];
-        if (n < nq + nk) {
+      // q and k columns, row-major (consecutive threads write consecutive dims)
+      if (n0 < nq + nk) {
+        for (int e = tid; e < BM * BN; e += NT) {
+          const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
+          if (m >= M || n >= a.N || n >= nq + nk) continue;
+          const int b = m / rs.nR, p = rs.start + m % rs.nR;
+          const int i = n % hd;
+          const float x = Ct[r * ldc + c];
           const int j = i < half ? i : i - half;
           const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angle of the slot's position
-        const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
+          const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
           const float y = i < half ? x * cs - Ct[r * ldc + c + half] * sn
                                    : x * cs + Ct[r * ldc + c - half] * sn;
           if (n < nq) {
@@ -173,7 +174,16 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
             const int kvh = (n - nq) / hd;
             store_val<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
           }
-        } else {
+        }
+      }
+      // v columns, row-fastest: consecutive threads write consecutive positions of one dim, which
+      // are adjacent in the transposed cache
+      if (n0 + BN > nq + nk) {
+        for (int e = tid; e < BM * BN; e += NT) {
+          const int r = e % BM, c = e / BM, m = m0 + r, n = n0 + c;
+          if (m >= M || n >= a.N || n < nq + nk) continue;
+          const int b = m / rs.nR, p = rs.start + m % rs.nR;
+          const int i = n % hd;
           const int kvh = (n - nq - nk) / hd;
           // V^T per (batch row, K/V head): fp32 [hd][Lp]; bf16 in 32-key tiles [Lp/32][hd][32], so
           // that the attention's key tile is one contiguous run per plane, with the keys of a tile
@@ -181,7 +191,7 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
           const size_t base = ((size_t)b * Hkv + kvh) * hd * rs.Lp;
           const size_t vi = sizeof(T) == 2 ? base + (size_t)(p >> 5) * hd * 32 + i * 32 + vt_key_pos(p & 31)
                                            : base + (size_t)i * rs.Lp + p;
-          store_val<T>(a.vt_cache, a.vt_cache_lo, vi, x);
+          store_val<T>(a.vt_cache, a.vt_cache_lo, vi, Ct[r * ldc + c]);
         }
       }
     } break;
