@@ -109,7 +109,8 @@ template <int HD>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
-    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part) {
+    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part,
+    int o_packed) {
   constexpr int KS = HD / 16;  // k-steps of the QK^T product
   constexpr int DB = HD / 32;  // 32-dim blocks of the output
   const int G = H / Hkv;
@@ -256,8 +257,10 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   // o[d][i]: dim d*32 + 8*(i/4) + 4*half + i%4 of query col
   if (gridDim.z == 1) {
     const float inv = 1.0f / lsum;
-    bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
-    bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
+    // output row m, columns head * HD + dim (panel-packed for a tiled output projection)
+    const size_t obase = o_packed ? pa_off(m, head * HD, ldq) : (size_t)m * ldq + head * HD;
+    bf16 *oh = o_hi + obase;
+    bf16 *ol = o_lo + obase;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -265,8 +268,9 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
         const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
         const float v = o[d][i] * inv;
         const bf16 hi = __float2bfloat16(v);
-        oh[dim] = hi;
-        ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+        const size_t od = o_packed ? (size_t)(dim >> 5) * 4096 + (dim & 31) : (size_t)dim;
+        oh[od] = hi;
+        ol[od] = __float2bfloat16(v - __bfloat162float(hi));
       }
   } else {
     // part[split][bg][qt][col][HD + 2]
@@ -301,7 +305,8 @@ template <int HD>
 __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
-    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part) {
+    RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part,
+    int o_packed) {
   constexpr int KS = HD / 16, DB = HD / 32;
   constexpr int PLANE = 32 * HD * 2;          // bytes of one plane of a 32-key tile
   constexpr int SLOT = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
@@ -514,8 +519,10 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   if (!valid) return;
   if (gridDim.z == 1) {
     const float inv = 1.0f / lsum;
-    bf16 *oh = o_hi + (size_t)m * ldq + head * HD;
-    bf16 *ol = o_lo + (size_t)m * ldq + head * HD;
+    // output row m, columns head * HD + dim (panel-packed for a tiled output projection)
+    const size_t obase = o_packed ? pa_off(m, head * HD, ldq) : (size_t)m * ldq + head * HD;
+    bf16 *oh = o_hi + obase;
+    bf16 *ol = o_lo + obase;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -523,8 +530,9 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
         const int dim = d * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
         const float v = o[d][i] * inv;
         const bf16 hi = __float2bfloat16(v);
-        oh[dim] = hi;
-        ol[dim] = __float2bfloat16(v - __bfloat162float(hi));
+        const size_t od = o_packed ? (size_t)(dim >> 5) * 4096 + (dim & 31) : (size_t)dim;
+        oh[od] = hi;
+        ol[od] = __float2bfloat16(v - __bfloat162float(hi));
       }
   } else {
     // part[split][bg][qt][col][HD + 2], as the few-query kernel writes it
@@ -547,7 +555,8 @@ template <int HD>
 __global__ __launch_bounds__(64 * MG_ROWS) void attn_merge_kernel(const float *__restrict__ part,
                                                                   RowSet rs, int H, int Hkv,
                                                                   int n_qt, int splits,
-                                                                  bf16 *o_hi, bf16 *o_lo) {
+                                                                  bf16 *o_hi, bf16 *o_lo,
+                                                                  int o_packed) {
   const int G = H / Hkv;
   const int slot = blockIdx.x * MG_ROWS + (threadIdx.x >> 6);  // (bg, qt, col)
   if (slot >= rs.B * Hkv * n_qt * 32) return;
@@ -594,7 +603,8 @@ __global__ __launch_bounds__(64 * MG_ROWS) void attn_merge_kernel(const float *_
       if (w[s] != 0.f) acc += v[s][j] * w[s];
     const float val = acc * inv;
     if (!dim_ok) break;
-    const size_t o = (size_t)m * H * HD + head * HD + lane + 64 * j;
+    const size_t o = o_packed ? pa_off(m, head * HD + lane + 64 * j, H * HD)
+                              : (size_t)m * H * HD + head * HD + lane + 64 * j;
     const bf16 hi = __float2bfloat16(val);
     o_hi[o] = hi;
     o_lo[o] = __float2bfloat16(val - __bfloat162float(hi));
@@ -644,8 +654,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
 hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache,
                             const void *k_cache_lo, const void *vt_cache, const void *vt_cache_lo,
                             RowSet rs, int H, int Hkv, int hd, bf16 *o_hi, bf16 *o_lo, float *o_f32,
-                            float *part, int dtype, hipStream_t st) {
+                            float *part, int dtype, int o_packed, hipStream_t st) {
   if (rs.M() <= 0) return hipSuccess;
+  if (o_packed && (dtype == 0 || (H * hd) % 32 || hd % 32)) return hipErrorInvalidValue;
   if (dtype == 0) {
     dim3 grid(rs.M(), H);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), rs.Lp * sizeof(float), st,
@@ -667,12 +678,12 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
     hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES), 0, st, (const bf16 *)q, \
                        (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,      \
                        (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, wchunk,    \
-                       scale_log2, o_hi, o_lo, part);                                            \
+                       scale_log2, o_hi, o_lo, part, o_packed);                                  \
     if (wsplits > 1)                                                                             \
       hipLaunchKernelGGL(attn_merge_kernel<HDV>,                                                 \
                          dim3((rs.B * Hkv * groups * AW_WAVES * 32 + MG_ROWS - 1) / MG_ROWS),    \
                          dim3(64 * MG_ROWS), 0, st, (const float *)part, rs, H, Hkv,             \
-                         groups * AW_WAVES, wsplits, o_hi, o_lo);                                \
+                         groups * AW_WAVES, wsplits, o_hi, o_lo, o_packed);                      \
     break;
     switch (hd) {
       ATTNW_CASE(32)
@@ -692,11 +703,11 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
     hipLaunchKernelGGL(attn_mfma_kernel<HDV>, grid, dim3(64), 0, st, (const bf16 *)q,           \
                        (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,     \
                        (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, chunk,    \
-                       scale_log2, o_hi, o_lo, part);                                           \
+                       scale_log2, o_hi, o_lo, part, o_packed);                                 \
     if (splits > 1)                                                                             \
       hipLaunchKernelGGL(attn_merge_kernel<HDV>, dim3((rs.B * Hkv * nqt * 32 + MG_ROWS - 1) / MG_ROWS), \
                          dim3(64 * MG_ROWS), 0, st, (const float *)part, rs, H, Hkv, nqt, splits, \
-                         o_hi, o_lo);                                                           \
+                         o_hi, o_lo, o_packed);                                                 \
     break;
   switch (hd) {
     ATTN_CASE(32)

@@ -100,6 +100,12 @@ struct Plan {
   int n_vtiles;
 };
 
+// Virtual width of the fused gate/up GEMM over M rows: gate and up rows interleaved per half tile.
+int gateup_width(const Plan &p, int M) {
+  const int bn = gemm_bn(M, p.dt);
+  return 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
+}
+
 // Rows [start, start + nR) of every batch row, over the full context.
 RowSet rows_of(const Plan &p, int start, int nR) {
   RowSet r;
@@ -160,9 +166,7 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   }
   size_t gpart = 0, apart = 0;
   for (int M : Ms) {
-    const int bn = gemm_bn(M, p.dt);
-    const int ffn_virtual = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
-    const int shapes[4][2] = {{p.nq + 2 * p.nkv, p.d}, {p.d, p.nq}, {ffn_virtual, p.d}, {p.d, p.F}};
+    const int shapes[4][2] = {{p.nq + 2 * p.nkv, p.d}, {p.d, p.nq}, {gateup_width(p, M), p.d}, {p.d, p.F}};
     for (auto &s : shapes) gpart = std::max(gpart, gemm_partial_bytes(M, s[0], s[1], p.dt));
     const int nR = M / p.B;
     apart = std::max(apart, attention_part_bytes(rows_of(p, 0, nR), p.H, p.Hkv, p.hd, p.dt));
@@ -195,11 +199,13 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_h = take(Mmax * p.d * 4);
   // GEMM input a: RMSNorm(h) [Mmax][d] or the attention output [Mmax][nq]; bf16 hi/lo planes,
   // or fp32 in the hi slot
-  const size_t wa = std::max(p.d, p.nq);
-  p.off_ahi = take(Mmax * wa * (p.dt ? 2 : 4));
-  p.off_alo = take(p.dt ? Mmax * wa * 2 : 0);
-  p.off_acthi = take(Mmax * p.F * (p.dt ? 2 : 4));
-  p.off_actlo = take(p.dt ? Mmax * p.F * 2 : 0);
+  // (bf16 planes are panel-packed, 128-row panels, when their consumer GEMM is tiled: rows are
+  // allocated up to the next multiple of 128)
+  const size_t wa = std::max(p.d, p.nq), Mpad = (Mmax + 127) / 128 * 128;
+  p.off_ahi = take(Mpad * wa * (p.dt ? 2 : 4));
+  p.off_alo = take(p.dt ? Mpad * wa * 2 : 0);
+  p.off_acthi = take(Mpad * p.F * (p.dt ? 2 : 4));
+  p.off_actlo = take(p.dt ? Mpad * p.F * 2 : 0);
   p.off_q = take(Mmax * p.nq * 4);  // fp32, or bf16 hi plane + lo plane
   p.off_apart = take(apart);
   p.off_gpart = take(gpart);
@@ -358,6 +364,13 @@ void *kv_layer_lo(dllm_t *h, char *base, int l) {
 }
 void *q_lo(dllm_t *h) { return (char *)h->q + h->p.Mmax * h->p.nq * 2; }
 
+// Whether the activations that feed an M x N x K GEMM are written panel-packed (the producer
+// asks about its consumer's shape).
+int a_packed(const dllm_t *h, int M, int N, int K) {
+  return h->p.dt == 1 && gemm_a_packed(M, N, K, 1);
+}
+
+
 GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M, int N, int K) {
   GemmArgs g;
   memset(&g, 0, sizeof g);
@@ -368,6 +381,7 @@ GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M
     g.a_f32 = (const float *)a_hi;
   }
   g.lda = lda;
+  g.a_packed = a_packed(h, M, N, K);
   g.M = M; g.N = N; g.K = K;
   g.partial = h->gpart;
   g.scale = 1.f;
@@ -380,8 +394,9 @@ void set_resid(dllm_t *h, GemmArgs &g, float *hres) {
   g.ld_out = h->p.d;
 }
 
-// Residual GEMM followed by the split-K fold and the next RMSNorm (gain) into a.
-int resid_gemm_norm(dllm_t *h, GemmArgs &g, const void *gain) {
+// Residual GEMM followed by the split-K fold and the next RMSNorm (gain) into a, which feeds a
+// GEMM of next_m rows and next_n columns (K = d).
+int resid_gemm_norm(dllm_t *h, GemmArgs &g, const void *gain, int next_m, int next_n) {
   const Plan &p = h->p;
   const bool bf = p.dt == 1;
   int splits = 1;
@@ -390,7 +405,7 @@ int resid_gemm_norm(dllm_t *h, GemmArgs &g, const void *gain) {
   HIPCHK(launch_resid_norm(g.M, p.d, g.resid, splits > 1 ? h->gpart : nullptr, splits > 1 ? splits : 0,
                            gain, h->cfg.rms_eps, bf ? (bf16 *)h->a_hi : nullptr,
                            bf ? (bf16 *)h->a_lo : nullptr, bf ? nullptr : (float *)h->a_hi, p.dt,
-                           h->st));
+                           a_packed(h, next_m, next_n, p.d), h->st));
   return DLLM_OK;
 }
 
@@ -405,7 +420,9 @@ int forward(dllm_t *h, RowSet rs) {
   bf16 *ahi = (bf16 *)h->a_hi, *alo = (bf16 *)h->a_lo;
   float *af = (float *)h->a_hi;
   HIPCHK(launch_embed_norm(h->x, h->embed, LW(h, 0, 0), rs, p.d, c.rms_eps, h->h, bf ? ahi : nullptr,
-                           bf ? alo : nullptr, bf ? nullptr : af, p.dt, h->st));
+                           bf ? alo : nullptr, bf ? nullptr : af, p.dt,
+                           a_packed(h, rs.M(), p.nq + 2 * p.nkv, p.d),
+                           h->st));
   const int s_blk = p.P + h->block * p.Bs;
   const bool narrow = h->block >= 0 && !(rs.start == s_blk && rs.nR == p.Bs) &&
                       rs.start <= s_blk && s_blk + p.Bs <= rs.start + rs.nR;
@@ -461,7 +478,7 @@ int forward(dllm_t *h, RowSet rs) {
                               bf ? kv_layer_lo(h, h->kc, l) : nullptr, kv_layer(h, h->vc, l),
                               bf ? kv_layer_lo(h, h->vc, l) : nullptr, lrs, p.H, p.Hkv, p.hd,
                               bf ? ahi : nullptr, bf ? alo : nullptr, bf ? nullptr : af, h->apart,
-                              p.dt, h->st));
+                              p.dt, a_packed(h, M, p.d, p.nq), h->st));
       if (ee) {
         HIPCHK(hipEventRecord(ee, h->st));
         // K and V of every cached position once per (batch row, K/V head), q in, o out
@@ -476,19 +493,18 @@ int forward(dllm_t *h, RowSet rs) {
       g.w[0] = LW(h, l, 4); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
       g.wp = WP(h, l, 1);
       set_resid(h, g, hres);
-      int rc = resid_gemm_norm(h, g, LW(h, l, 5));
+      int rc = resid_gemm_norm(h, g, LW(h, l, 5), M, gateup_width(p, M));
       if (rc) return rc;
     }
     // gate/up + SwiGLU -> act
     {
-      const int bn = gemm_bn(M, p.dt);
-      const int nvirt = 2 * ((p.F + bn / 2 - 1) / (bn / 2)) * (bn / 2);
-      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, nvirt, p.d);
+      GemmArgs g = gemm_base(h, h->a_hi, h->a_lo, p.d, M, gateup_width(p, M), p.d);
       g.w[0] = LW(h, l, 6); g.w[1] = LW(h, l, 7);
       g.wp = WP(h, l, 2);
       g.n_half = p.F;
       g.epi = EPI_SWIGLU;
       g.ld_act = p.F;
+      g.act_packed = a_packed(h, M, p.d, p.F);
       if (bf) { g.act_hi = (bf16 *)h->act_hi; g.act_lo = (bf16 *)h->act_lo; }
       else g.act_f32 = (float *)h->act_hi;
       int rc = run_gemm(h, g, 2 * p.F, 4.0 * M * p.F, nullptr);  // act as a 4-byte pair
@@ -500,7 +516,10 @@ int forward(dllm_t *h, RowSet rs) {
       g.w[0] = LW(h, l, 8); g.seg_end[0] = p.d; g.seg_end[1] = g.seg_end[2] = p.d;
       g.wp = WP(h, l, 3);
       set_resid(h, g, hres);
-      int rc = resid_gemm_norm(h, g, l + 1 < c.n_layers ? LW(h, l + 1, 0) : h->final_norm);
+      // the next layer's Q/K/V projection takes rs's rows, the lm_head the block rows
+      const bool last = l + 1 == c.n_layers;
+      int rc = resid_gemm_norm(h, g, last ? h->final_norm : LW(h, l + 1, 0),
+                               last ? p.B * p.Bs : rs.M(), last ? p.V : p.nq + 2 * p.nkv);
       if (rc) return rc;
     }
   }

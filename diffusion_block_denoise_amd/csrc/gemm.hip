@@ -202,7 +202,7 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
         const int r = e / half, c = e % half, m = m0 + r, f = f0 + c;
         if (m >= M || f >= a.n_half) continue;
         const float y = silu_f(Ct[r * ldc + c]) * Ct[r * ldc + c + half];
-        const size_t o = (size_t)m * a.ld_act + f;
+        const size_t o = a.act_packed ? pa_off(m, f, a.ld_act) : (size_t)m * a.ld_act + f;
         if (a.act_f32) {
           a.act_f32[o] = y;
         } else {
@@ -524,7 +524,8 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < IR; ++j) {
     const int pos = (wave * IR + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
-    aoff[j] = (size_t)a_row(a, min(m0 + r, a.M - 1)) * a.lda + c * 8;
+    const size_t row = a_row(a, min(m0 + r, a.M - 1));
+    aoff[j] = a.a_packed ? pa_off(row, c * 8, a.K) : row * a.lda + c * 8;
     wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
   }
   const uint16_t *ahi = (const uint16_t *)a.a_hi, *alo = (const uint16_t *)a.a_lo;
@@ -534,10 +535,11 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
     const int k0 = kbeg + min(t, T - 1) * BG_BK;
     unsigned char *st = smem + (t % BG_NS) * STAGE + wave * (IR * 1024);
     const size_t kw = (size_t)(k0 / PW_K) * (PW_ROWS * PW_K);
+    const size_t ka = a.a_packed ? kw : (size_t)k0;  // packed A: 32-wide blocks like W
 #pragma unroll
     for (int j = 0; j < IR; ++j) {
-      __builtin_amdgcn_global_load_lds((const void *)(ahi + aoff[j] + k0), (lds_void *)(st + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(alo + aoff[j] + k0), (lds_void *)(st + REG + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(ahi + aoff[j] + ka), (lds_void *)(st + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(alo + aoff[j] + ka), (lds_void *)(st + REG + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void *)(wsrc[j] + kw), (lds_void *)(st + 2 * REG + j * 1024), 16, 0, 0);
     }
   };
@@ -996,6 +998,8 @@ size_t gemm_partial_bytes(int M, int N, int K, int dtype) {
   return (size_t)pl.splits * M * (N - pl.n_tail0) * sizeof(float);
 }
 
+bool gemm_a_packed(int M, int N, int K, int dtype) { return choose_kind(M, N, K, dtype) == GK_BIG; }
+
 int gemm_kind(int M, int K, int dtype) {
   if (dtype == 0) return 0;
   return use_skinny(M, K) ? 1 : 2;
@@ -1006,6 +1010,10 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   GemmArgs a = a0;
   if (splits_out) *splits_out = 1;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  // panel-packed A only for the large-tile kernel; a packed SwiGLU output needs whole k blocks
+  if ((a.a_packed && !gemm_a_packed(a.M, a.N, a.K, dtype)) ||
+      (a.epi == EPI_SWIGLU && a.act_packed && (dtype == 0 || a.ld_act % 32)))
+    return hipErrorInvalidValue;
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
   if (dtype == 0) {

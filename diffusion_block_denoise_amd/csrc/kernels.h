@@ -45,6 +45,16 @@ __host__ __device__ inline int vt_key_pos(int k) {
   return ((k >> 4) * 2 + ((k >> 2) & 1)) * 8 + ((k >> 3) & 1) * 4 + (k & 3);
 }
 
+// Panel-packed activations: the hi/lo A operand of the large-tile GEMM is stored like the packed
+// weights, element (m, k) of an M x K matrix at
+// ((m / 128) * (K / 32) + k / 32) * 4096 + (m % 128) * 32 + k % 32 (K a multiple of 32, rows
+// padded to a multiple of 128), so a 32-wide k block of a 128-row tile is one contiguous 8 KB
+// run.  The other GEMMs read row-major activations (the 128-row tiled kernel, which loads A
+// through registers, measured slower on the packed layout).
+__host__ __device__ inline size_t pa_off(size_t m, int k, int K) {
+  return ((m >> 7) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 4096 + (m & 127) * 32 + (k & 31);
+}
+
 // GEMM epilogues.  The GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (fp32 accumulate).
 enum Epi : int {
   EPI_STORE = 0,   // out_f32[m*ld_out + n] = scale * C
@@ -67,10 +77,13 @@ struct GemmArgs {
   // (m / row_per) * row_stride + row_off + m % row_per of the array (row_per 0: row m).
   //   bf16 path: a_hi + a_lo (two bf16 arrays whose sum is the fp32 activation)
   //   f32 path : a_f32
+  // a_packed: the hi/lo planes are panel-packed (pa_off with K columns; lda unused); taken by
+  // the large-tile kernel only, and exactly when gemm_a_packed says so.
   const bf16 *a_hi, *a_lo;
   const float *a_f32;
   int lda;
   int row_per, row_stride, row_off;
+  int a_packed;
   // W operand: N x K rows from up to three segments (torch Linear layout, ld = K).
   // Plain mode: virtual row n lives in segment s with seg_end[s-1] <= n < seg_end[s].
   // SwiGLU mode: tile t, column c < BN/2 -> gate row t*BN/2 + c; else up row t*BN/2 + c - BN/2,
@@ -105,8 +118,8 @@ struct GemmArgs {
   // f32 path: one fp32 array each.  bf16 path: a hi and a lo bf16 plane each (hi + lo = value).
   void *q_out, *q_out_lo;
   void *k_cache, *k_cache_lo, *vt_cache, *vt_cache_lo;
-  // SWIGLU output (bf16 path: hi/lo; f32 path: f32), ld = ld_act
-  bf16 *act_hi, *act_lo; float *act_f32; int ld_act;
+  // SWIGLU output (bf16 path: hi/lo, panel-packed when act_packed; f32 path: f32), ld = ld_act
+  bf16 *act_hi, *act_lo; float *act_f32; int ld_act; int act_packed;
   // LMHEAD
   HeadPart *head_part; int n_vtiles; int vocab; int mask_id;
 };
@@ -129,6 +142,10 @@ hipError_t launch_gemm(const GemmArgs &a, int dtype, hipStream_t st, int *splits
                        hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 // Which kernel launch_gemm uses: 0 = f32 SIMT, 1 = skinny weight-streaming, 2 = tiled MFMA.
 int gemm_kind(int M, int K, int dtype);
+// Whether the A operand of an M x N x K GEMM is read panel-packed (when launch_gemm runs it on
+// the large-tile kernel, whose LDS-DMA stages then take whole 512-byte runs of A): the producers
+// of activations write that layout exactly when their consumer's answer is yes.
+bool gemm_a_packed(int M, int N, int K, int dtype);
 // Tile width (N direction) that launch_gemm uses for a given M and dtype; SwiGLU and
 // the lm_head partial layout depend on it.
 int gemm_bn(int M, int dtype);
@@ -137,21 +154,25 @@ int gemm_bn(int M, int dtype);
 int gemm_num_splits(int M, int N, int K, int dtype);
 size_t gemm_partial_bytes(int M, int N, int K, int dtype);
 
-// h[m] = embed[x[b][p]] (fp32); a = RMSNorm(h[m]) * gain as hi/lo planes (bf16) or f32.
+// h[m] = embed[x[b][p]] (fp32); a = RMSNorm(h[m]) * gain as hi/lo planes (bf16; panel-packed
+// when a_packed) or f32.
 hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rows, int d,
                              float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
-                             hipStream_t st);
+                             int a_packed, hipStream_t st);
 // Per row m < M: h[m] += sum over the splits of partial[z][m] (in split order; splits 0: no
-// partials), then a[m] = RMSNorm(h[m]) * gain as hi/lo planes (bf16) or f32.
+// partials), then a[m] = RMSNorm(h[m]) * gain as hi/lo planes (bf16; panel-packed when
+// a_packed) or f32.
 hipError_t launch_resid_norm(int M, int d, float *h, const float *partial, int splits,
                              const void *gain, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32,
-                             int dtype, hipStream_t st);
+                             int dtype, int a_packed, hipStream_t st);
 // Non-causal attention of the rows' queries over all L cached positions.
-// bf16 path: q, K and V^T come as hi/lo plane pairs; f32 path: the *_lo pointers are unused.
+// bf16 path: q, K and V^T come as hi/lo plane pairs, the output o as hi/lo planes [M][H * hd]
+// (panel-packed when o_packed); f32 path: the *_lo pointers are unused.
 hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache,
                             const void *k_cache_lo, const void *vt_cache, const void *vt_cache_lo,
                             RowSet rows, int n_heads, int n_kv_heads, int head_dim, bf16 *o_hi,
-                            bf16 *o_lo, float *o_f32, float *part, int dtype, hipStream_t st);
+                            bf16 *o_lo, float *o_f32, float *part, int dtype, int o_packed,
+                            hipStream_t st);
 size_t attention_part_bytes(RowSet rows, int n_heads, int n_kv_heads, int head_dim, int dtype);
 // Merge lm_head partials: tok, conf = 1/Z, p2 = exp(m2 - m1)/Z per row.
 hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,

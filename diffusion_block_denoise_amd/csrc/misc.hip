@@ -56,7 +56,7 @@ template <typename T>
 __global__ __launch_bounds__(RN_NT) void embed_norm_kernel(const int *x, const T *embed,
                                                            const T *gain, RowSet rs, int d,
                                                            float eps, float *h, bf16 *a_hi,
-                                                           bf16 *a_lo, float *a_f32) {
+                                                           bf16 *a_lo, float *a_f32, int a_packed) {
   const int m = blockIdx.x;
   const int b = m / rs.nR, p = rs.start + m % rs.nR;
   const int tok = x[(size_t)b * rs.Lx + rs.pos(p)];
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(RN_NT) void embed_norm_kernel(const int *x, const T
 #pragma unroll
   for (int c = 0; c < RN_MAX_C; ++c) {
     const int i = (c * RN_NT + threadIdx.x) * 4;
-    if (i < d) norm_store4<T>(v[c], r, gain, (size_t)m * d + i, i, a_hi, a_lo, a_f32);
+    if (i < d) norm_store4<T>(v[c], r, gain, a_packed ? pa_off(m, i, d) : (size_t)m * d + i, i, a_hi, a_lo, a_f32);
   }
 }
 
@@ -85,7 +85,8 @@ template <typename T>
 __global__ __launch_bounds__(RN_NT) void resid_norm_kernel(int M, int d, float *h,
                                                            const float *__restrict__ part,
                                                            int splits, const T *gain, float eps,
-                                                           bf16 *a_hi, bf16 *a_lo, float *a_f32) {
+                                                           bf16 *a_hi, bf16 *a_lo, float *a_f32,
+                                                           int a_packed) {
   const int m = blockIdx.x;
   const size_t MD = (size_t)M * d;
   float4 v[RN_MAX_C];
@@ -110,35 +111,37 @@ __global__ __launch_bounds__(RN_NT) void resid_norm_kernel(int M, int d, float *
 #pragma unroll
   for (int c = 0; c < RN_MAX_C; ++c) {
     const int i = (c * RN_NT + threadIdx.x) * 4;
-    if (i < d) norm_store4<T>(v[c], r, gain, (size_t)m * d + i, i, a_hi, a_lo, a_f32);
+    if (i < d) norm_store4<T>(v[c], r, gain, a_packed ? pa_off(m, i, d) : (size_t)m * d + i, i, a_hi, a_lo, a_f32);
   }
 }
 
 hipError_t launch_embed_norm(const int *x, const void *embed, const void *gain, RowSet rs, int d,
                              float eps, float *h, bf16 *a_hi, bf16 *a_lo, float *a_f32, int dtype,
-                             hipStream_t st) {
+                             int a_packed, hipStream_t st) {
   if (rs.M() <= 0) return hipSuccess;
-  if (d % 4 || d > RN_NT * 4 * RN_MAX_C) return hipErrorInvalidValue;
+  if (d % 4 || d > RN_NT * 4 * RN_MAX_C || (a_packed && (dtype == 0 || d % 32)))
+    return hipErrorInvalidValue;
   if (dtype == 0)
     hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(rs.M()), dim3(RN_NT), 0, st, x,
-                       (const float *)embed, (const float *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
+                       (const float *)embed, (const float *)gain, rs, d, eps, h, a_hi, a_lo, a_f32, 0);
   else
     hipLaunchKernelGGL(embed_norm_kernel<bf16>, dim3(rs.M()), dim3(RN_NT), 0, st, x,
-                       (const bf16 *)embed, (const bf16 *)gain, rs, d, eps, h, a_hi, a_lo, a_f32);
+                       (const bf16 *)embed, (const bf16 *)gain, rs, d, eps, h, a_hi, a_lo, a_f32, a_packed);
   return hipGetLastError();
 }
 
 hipError_t launch_resid_norm(int M, int d, float *h, const float *partial, int splits,
                              const void *gain, float eps, bf16 *a_hi, bf16 *a_lo, float *a_f32,
-                             int dtype, hipStream_t st) {
+                             int dtype, int a_packed, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if (d % 4 || d > RN_NT * 4 * RN_MAX_C) return hipErrorInvalidValue;
+  if (d % 4 || d > RN_NT * 4 * RN_MAX_C || (a_packed && (dtype == 0 || d % 32)))
+    return hipErrorInvalidValue;
   if (dtype == 0)
     hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(M), dim3(RN_NT), 0, st, M, d, h, partial,
-                       splits, (const float *)gain, eps, a_hi, a_lo, a_f32);
+                       splits, (const float *)gain, eps, a_hi, a_lo, a_f32, 0);
   else
     hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(M), dim3(RN_NT), 0, st, M, d, h, partial,
-                       splits, (const bf16 *)gain, eps, a_hi, a_lo, a_f32);
+                       splits, (const bf16 *)gain, eps, a_hi, a_lo, a_f32, a_packed);
   return hipGetLastError();
 }
 
