@@ -286,35 +286,44 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   }
 }
 
-// Many-query variant (block refresh): 4 waves per workgroup, one 32-query tile each, all of the
-// same (batch row, K/V head).  The 32-key tiles of K and V^T (hi and lo) go straight from global
-// memory into a ring of 3 LDS slots (global_load_lds, 16 bytes per lane, no register staging),
-// two tiles ahead, one barrier per tile; every wave runs the per-wave kernel's MFMA sequence
-// with its operands read from LDS.  In a slot, row r's 16-byte chunk c sits at chunk position
-// r * CPR + (c ^ f(r)) (CPR chunks per row: f(r) = r & 15 for 16, (r >> 1) & 7 for 8,
+// Many-query variant (block refresh): 8 waves per workgroup, all of the same (batch row, K/V
+// head): 4 query tiles of 32 queries, each run by two waves that take alternate 32-key tiles
+// (key half 0 the even ones, key half 1 the odd ones), so every SIMD holds two waves and one
+// wave's MFMAs overlap the other's softmax and LDS reads.  Each iteration brings one pair of
+// key tiles (K and V^T, hi and lo) straight from global memory into one of two LDS slots
+// (global_load_lds, 16 bytes per lane, no register staging) while the waves work on the other
+// slot; one barrier per iteration.  At the end the two waves of a query tile merge their
+// (reference maximum, sum, output) through LDS.  In a tile, row r's 16-byte chunk c sits at chunk
+// position r * CPR + (c ^ f(r)) (CPR chunks per row: f(r) = r & 15 for 16, (r >> 1) & 7 for 8,
 // (r >> 2) & 3 for 4), so the fragment reads of 16 consecutive rows cover the 64 banks (256
-// bytes) of the LDS once.  When the
-// workgroups cannot fill the GPU the keys are split into chunks (partials + the merge kernel).
-static constexpr int AW_WAVES = 4, AW_SLOTS = 4;
+// bytes) of the LDS once.  When the workgroups cannot fill the GPU the keys are split into chunks
+// (partials + the merge kernel).
+static constexpr int AW_WAVES = 4, AW_KH = 2;  // query tiles per workgroup, key halves
 
 __device__ inline int aw_swz(int r, int cpr) {
   return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 template <int HD>
-__global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
+__global__ __launch_bounds__(64 * AW_WAVES * AW_KH, 1) void attn_wide_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
     RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part,
     int o_packed) {
   constexpr int KS = HD / 16, DB = HD / 32;
   constexpr int PLANE = 32 * HD * 2;          // bytes of one plane of a 32-key tile
-  constexpr int SLOT = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
-  constexpr int LPW = SLOT / 1024 / AW_WAVES; // 1 KB loads per wave per tile
+  constexpr int TILE = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
+  constexpr int PAIR = AW_KH * TILE;          // the tiles of one iteration, one per key half
+  constexpr int NW = AW_WAVES * AW_KH;
+  constexpr int LPW = PAIR / 1024 / NW;       // 1 KB loads per wave per iteration
   constexpr int KCPR = HD / 8, VCPR = 4;      // 16-byte chunks per K row / per V^T row
-  static_assert(SLOT % (1024 * AW_WAVES) == 0 && LPW >= 1, "tile staging");
+  static_assert(PAIR % (1024 * NW) == 0 && LPW >= 1 && LPW <= 15, "tile staging");
+  static_assert(LPW * 64 * AW_WAVES == TILE / 16, "the waves of key half h load tile h");
+  // the merge of the key halves reuses the ring: outputs [query tile][d][i][lane], then
+  // (reference maximum, sum) [query tile][2][lane]
+  static_assert(AW_WAVES * (DB * 16 + 2) * 64 * 4 <= 2 * PAIR, "merge area");
   typedef __attribute__((address_space(3))) void lds_void;
-  __shared__ __align__(1024) unsigned char lds[AW_SLOTS * SLOT];
+  __shared__ __align__(1024) unsigned char lds[2 * PAIR];
 
   const int G = H / Hkv;
   const int nrows = rs.nR * G;
@@ -325,7 +334,8 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   const int n_qt = gridDim.x / ((npairs + 7) / 8 * 8) * AW_WAVES;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int qt = grp * AW_WAVES + wave;
+  const int qw = wave % AW_WAVES, kh = wave / AW_WAVES;
+  const int qt = grp * AW_WAVES + qw;
   const int r = qt * 32 + col;
   const bool valid = r < nrows;
   const int pi = valid ? r / G : 0;
@@ -343,11 +353,13 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   }
   // K [Lp][HD]; V^T in 32-key tiles [Lp/32][HD][32]: tile kb of either plane starts kb * HD in
   const size_t kv_off = (size_t)bg * rs.Lp * HD;
-  // load j of this wave fills chunk positions (wave * LPW + j) * 64 + lane of the slot
+  // load j of this wave fills chunk position e = (wave * LPW + j) * 64 + lane of the pair slot:
+  // tile e / (TILE / 16) = kh of the pair, then plane and position inside the tile
   const uint16_t *src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int e = (wave * LPW + j) * 64 + lane, plane = e / (PLANE / 16), pos = e % (PLANE / 16);
+    const int e = (wave * LPW + j) * 64 + lane, et = e % (TILE / 16);
+    const int plane = et / (PLANE / 16), pos = et % (PLANE / 16);
     const bf16 *base = plane == 0 ? k_hi : plane == 1 ? k_lo : plane == 2 ? vt_hi : vt_lo;
     int off;
     if (plane < 2) {
@@ -361,9 +373,10 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   }
   const int ntile = (rs.L + 31) / 32;
   const int t0 = split * (chunk / 32), t1 = min(ntile, t0 + chunk / 32), T = t1 - t0;
-  auto issue = [&](int u) {  // tile t0 + u (clamped to the last) into slot u % AW_SLOTS
-    const size_t kb = (size_t)(t0 + min(u, T - 1)) * 32;
-    unsigned char *dst = lds + (u % AW_SLOTS) * SLOT + wave * LPW * 1024;
+  const int NI = (T + AW_KH - 1) / AW_KH;  // iterations
+  auto issue = [&](int u) {  // tile t0 + 2u + kh (clamped to the last) into slot u % 2
+    unsigned char *dst = lds + (u & 1) * PAIR + wave * LPW * 1024;
+    const size_t kb = (size_t)(t0 + min(u * AW_KH + kh, T - 1)) * 32;
 #pragma unroll
     for (int j = 0; j < LPW; ++j)
       __builtin_amdgcn_global_load_lds((const void *)(src[j] + kb * HD), (lds_void *)(dst + j * 1024), 16, 0, 0);
@@ -379,111 +392,66 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
   // fragment positions (bytes in a plane): K row col, chunk 2 kk + half; V^T row d * 32 + col,
   // chunk 2 ks + half
   const int ksw = aw_swz(col, KCPR), krow = col * KCPR;
-  // S^T of one tile from its slot (all K fragments read before the first MFMA)
-  auto scores = [&](int u) {
-    const unsigned char *cur = lds + (u % AW_SLOTS) * SLOT;
-    bf16x8_t kh[KS], kl[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int pos = (krow + ((kk * 2 + half) ^ ksw)) * 16;
-      kh[kk] = *(const bf16x8_t *)(cur + pos);
-      kl[kk] = *(const bf16x8_t *)(cur + PLANE + pos);
-    }
-    f32x16 sc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], qh[kk], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], sc, 0, 0, 0);
-    }
-    return sc;
-  };
-  // tile u has landed once only tile u + 1's loads are outstanding (vmcnt(LPW)); the barrier
-  // also tells that every wave is done with the slot the next issue overwrites
-  auto land_and_sync = [&]() {
-    if constexpr (LPW == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-    else if constexpr (LPW == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-    else __builtin_amdgcn_s_waitcnt(0x0F72);
+  issue(0);
+  for (int u = 0; u < NI; ++u) {
+    // this wave's loads of pair u have landed (nothing else is outstanding); after the barrier
+    // every wave's have, and every wave is done with pair u - 1, whose slot the next issue fills
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-  };
-  // Software pipeline over the key tiles: the MFMAs of tile u + 1's scores are issued next to
-  // the softmax of tile u, so the matrix cores work while the wave's VALU computes the
-  // probabilities (one wave per SIMD: the softmax alone would leave the MFMA pipe idle).  Ring
-  // of 4 slots: at iteration u tiles u and u + 1 are resident, u + 2 is landing and u + 3 goes
-  // into the slot of tile u - 1, which every wave finished before this iteration's barrier; so
-  // tile u's V^T fragments can be read after the softmax (K and V^T fragments are never live
-  // together).
-  issue(0);
-  issue(1);
-  land_and_sync();  // tile 0
-  issue(2);
-  f32x16 sc = scores(0);
-  for (int u = 0; u < T; ++u) {
-    const int kb = (t0 + u) * 32;
-    // (the last iteration repeats the clamped tile's scores, unused, to keep the block straight)
-    land_and_sync();  // tile u + 1
-    issue(u + 3);     // into the slot of tile u - 1
+    if (u + 1 < NI) issue(u + 1);
+    const int tl = u * AW_KH + kh;  // this wave's tile, counted from t0
+    const bool tok = tl < T;        // the odd count's last pair has one tile
+    const int kb = (t0 + tl) * 32;
+    const unsigned char *cur = lds + (u & 1) * PAIR + kh * TILE;
     __builtin_amdgcn_sched_barrier(0);
-    // K fragments of tile u + 1 (all read before the first MFMA)
-    const unsigned char *nxt = lds + (min(u + 1, T - 1) % AW_SLOTS) * SLOT;
-    bf16x8_t kh[KS], kl[KS];
+    // S^T of the tile (32 keys x 32 queries), three terms of the hi/lo pairs
+    f32x16 sc;
+    {
+      bf16x8_t kfh[KS], kfl[KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const int pos = (krow + ((kk * 2 + half) ^ ksw)) * 16;
-      kh[kk] = *(const bf16x8_t *)(nxt + pos);
-      kl[kk] = *(const bf16x8_t *)(nxt + PLANE + pos);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // The score MFMAs of tile u + 1 (a dependent chain of 3 KS) interleaved with the softmax of
-    // tile u, one softmax step after each MFMA: the steps are independent of the chain, so the
-    // VALU works while the matrix core does.
-    f32x16 sn, sn1, sn2;  // three independent chains (hi K, lo K, lo q), summed at the end
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sn[i] = sn1[i] = sn2[i] = 0.f;
-    float tmax = -INFINITY, mnew = 0.f, alpha = 0.f, psum = 0.f;
-    bf16x8_t ph[2], pl[2];
-    auto step = [&](int k) {  // k: 0..15 mask and max; 16 row max; 17..32 exp; 33 sums
-      if (k < 16) {
-        const int key = kb + 8 * (k >> 2) + 4 * half + (k & 3);
-        sc[k] = key < klim ? sc[k] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sc[k]);
-      } else if (k == 16) {
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        mnew = ref_max(mrun, tmax);
-        alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
-      } else if (k < 33) {
-        const int i = k - 17;
-        const float pv = mnew == -INFINITY ? 0.f : exp2f(sc[i] - mnew);
-        const __bf16 hi = (__bf16)pv;
-        ph[i >> 3][i & 7] = hi;
-        pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
-        psum += pv;
-      } else {
-        psum += __shfl_xor(psum, 32, 64);
-        lsum = lsum * alpha + psum;
-        mrun = mnew;
+      for (int kk = 0; kk < KS; ++kk) {
+        const int pos = (krow + ((kk * 2 + half) ^ ksw)) * 16;
+        kfh[kk] = *(const bf16x8_t *)(cur + pos);
+        kfl[kk] = *(const bf16x8_t *)(cur + PLANE + pos);
       }
-    };
 #pragma unroll
-    for (int g = 0; g < 3 * KS; ++g) {
-      const int kk = g / 3, term = g % 3;
-      if (term == 0) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], qh[kk], sn, 0, 0, 0);
-      else if (term == 1) sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[kk], qh[kk], sn1, 0, 0, 0);
-      else sn2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[kk], ql[kk], sn2, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      step(g);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kk], qh[kk], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfl[kk], qh[kk], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfh[kk], ql[kk], sc, 0, 0, 0);
+      }
     }
+    // softmax against the reference maximum; lane (col, half) holds keys
+    // kb + 8 (k / 4) + 4 half + k % 4 of query col
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int g = 3 * KS; g < 34; ++g) step(g);
+    for (int k = 0; k < 16; ++k) {
+      const int key = kb + 8 * (k >> 2) + 4 * half + (k & 3);
+      sc[k] = tok && key < klim ? sc[k] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sc[k]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = ref_max(mrun, tmax);
+    const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+    bf16x8_t ph[2], pl[2];
+    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sn[i] = sn[i] + (sn1[i] + sn2[i]);
+    for (int i = 0; i < 16; ++i) {
+      const float pv = mnew == -INFINITY ? 0.f : exp2f(sc[i] - mnew);
+      const __bf16 hi = (__bf16)pv;
+      ph[i >> 3][i & 7] = hi;
+      pl[i >> 3][i & 7] = (__bf16)(pv - (float)hi);
+      psum += pv;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    lsum = lsum * alpha + psum;
+    mrun = mnew;
+    // V^T fragments only now: K and V^T fragments are never live together
     __builtin_amdgcn_sched_barrier(0);
-    const unsigned char *cur = lds + (u % AW_SLOTS) * SLOT;
     bf16x8_t vfh[DB][2], vfl[DB][2];
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
@@ -513,13 +481,37 @@ __global__ __launch_bounds__(64 * AW_WAVES, 1) void attn_wide_kernel(
 #pragma unroll
       for (int d = 0; d < DB; ++d) o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfh[d][ks], pl[ks], o[d], 0, 0, 0);
     }
-    sc = sn;
   }
+  // merge the key halves: half 1 hands its state to half 0 through the (now idle) ring
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
-  if (!valid) return;
+  __syncthreads();
+  float *xo = (float *)lds;
+  float *xm = xo + AW_WAVES * DB * 16 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xo[((qw * DB + d) * 16 + i) * 64 + lane] = o[d][i];
+    xm[(qw * 2) * 64 + lane] = mrun;
+    xm[(qw * 2 + 1) * 64 + lane] = lsum;
+  }
+  __syncthreads();
+  if (kh == 1 || !valid) return;
+  {
+    const float m2 = xm[(qw * 2) * 64 + lane], l2 = xm[(qw * 2 + 1) * 64 + lane];
+    const float mt = fmaxf(mrun, m2);
+    const float a1 = mrun == -INFINITY ? 0.f : exp2f(mrun - mt);
+    const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mt);
+    lsum = lsum * a1 + l2 * a2;
+    mrun = mt;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] = o[d][i] * a1 + xo[((qw * DB + d) * 16 + i) * 64 + lane] * a2;
+  }
   if (gridDim.z == 1) {
     const float inv = 1.0f / lsum;
-    // output row m, columns head * HD + dim (panel-packed for a tiled output projection)
+    // output row m, columns head * HD + dim (panel-packed for a large-tile output projection)
     const size_t obase = o_packed ? pa_off(m, head * HD, ldq) : (size_t)m * ldq + head * HD;
     bf16 *oh = o_hi + obase;
     bf16 *ol = o_lo + obase;
@@ -675,7 +667,8 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
     dim3 wgrid(attn_grid_x(rs.B * Hkv, groups), 1, wsplits);
 #define ATTNW_CASE(HDV)                                                                          \
   case HDV:                                                                                      \
-    hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES), 0, st, (const bf16 *)q, \
+    hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES * AW_KH), 0, st,          \
+                       (const bf16 *)q,                                                          \
                        (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,      \
                        (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, wchunk,    \
                        scale_log2, o_hi, o_lo, part, o_packed);                                  \
