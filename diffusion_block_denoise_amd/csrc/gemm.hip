@@ -909,13 +909,14 @@ static double cu_makespan(long n_full, int it_full, long n_tail, int it_tail, in
   return end;
 }
 
-static SplitPlan tile_plan(int kind, int M, int N, int K) {
+static SplitPlan tile_plan(int kind, int M, int N, int K, double *cost_out) {
   const bool big = kind == GK_BIG;
   const int bm = big ? 256 : 128, bn = big ? 256 : 128, per_cu = big ? 1 : 2;
   const double t1 = big ? 3.7 : 1.25, t2 = 1.98;
   const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn, iters = K / 64;
   const long tiles = (long)mt * nt;
   SplitPlan best_plan{kind, 1, K, (int)tiles, N};
+  *cost_out = -1.0;  // not modelled: many rounds of tiles
   // splits need whole columns in launch order: a single group of rows (tile_coords); with many
   // rounds of tiles the tail is negligible
   if (mt > (big ? BIG_GM : TILED_GM) || tiles > 16L * 256 * per_cu) return best_plan;
@@ -941,31 +942,46 @@ static SplitPlan tile_plan(int kind, int M, int N, int K) {
     }
   }
   if (best_plan.splits == 1) { best_plan.n_full = (int)tiles; best_plan.n_tail0 = N; }
+  *cost_out = best;
   return best_plan;
 }
 
-static int choose_kind(int M, int N, int K, int dtype) {
-  if (dtype == 0) return GK_F32;
-  if (use_skinny(M, K)) return GK_SKINNY;
-  const long big_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
-  if (M >= 512 && big_tiles >= 256 && K % 64 == 0) return GK_BIG;
-  return GK_TILED;
-}
-
 // The tile plans are computed once per shape (the list schedule takes up to a few ms).
-static SplitPlan tile_plan_cached(int kind, int M, int N, int K) {
+static SplitPlan tile_plan_cached(int kind, int M, int N, int K, double *cost_out = nullptr) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, int>, SplitPlan> cache;
+  static std::map<std::tuple<int, int, int, int>, std::pair<SplitPlan, double>> cache;
   const auto key = std::make_tuple(kind, M, N, K);
   {
     std::lock_guard<std::mutex> lk(mu);
     auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
+    if (it != cache.end()) {
+      if (cost_out) *cost_out = it->second.second;
+      return it->second.first;
+    }
   }
-  const SplitPlan pl = tile_plan(kind, M, N, K);
+  double cost;
+  const SplitPlan pl = tile_plan(kind, M, N, K, &cost);
   std::lock_guard<std::mutex> lk(mu);
-  cache.emplace(key, pl);
+  cache.emplace(key, std::make_pair(pl, cost));
+  if (cost_out) *cost_out = cost;
   return pl;
+}
+
+// Kernel of a bf16 GEMM of more than 64 rows: the large-tile kernel when its 256 x 256 tiles
+// fill the CUs at least once; with fewer, the one whose split plan the CU schedule model prices
+// lower (the large-tile kernel within 2 %: at 768 rows it measured faster than the model says on
+// the output and down projections, and slower on q/k/v, as the model has it).
+static int choose_kind(int M, int N, int K, int dtype) {
+  if (dtype == 0) return GK_F32;
+  if (use_skinny(M, K)) return GK_SKINNY;
+  if (M < 512 || K % 64) return GK_TILED;
+  const long big_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 256) return GK_BIG;
+  double c_tiled, c_big;
+  tile_plan_cached(GK_TILED, M, N, K, &c_tiled);
+  tile_plan_cached(GK_BIG, M, N, K, &c_big);
+  if (c_tiled < 0 || c_big < 0) return GK_TILED;  // many row tiles: not modelled
+  return c_big <= 1.02 * c_tiled ? GK_BIG : GK_TILED;
 }
 
 static SplitPlan split_plan(int M, int N, int K, int dtype) {
