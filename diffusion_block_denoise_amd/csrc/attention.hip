@@ -47,15 +47,19 @@ static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk)
   splits = (kt * 32 + chunk - 1) / chunk;
 }
 
-// Many-query kernel (4 query tiles per workgroup, one workgroup per CU): split the keys only
-// when the workgroups fill less than half of the 256 CUs.  A workgroup's time per key tile
-// hardly changes with the number of workgroups (measured: 768 queries x 32 heads, 192
-// workgroups, 79 us whole; 4 chunks 70 us plus 21 us to merge), so splitting pays only when
-// most CUs would idle.
-static constexpr int AW_GROUP = 4;  // query tiles per workgroup (the kernel's waves)
+// Query tiles per workgroup of the many-query kernel for nqt query tiles per (batch row, K/V
+// head): 4, or 2 for two or three (then a pair's K/V tiles still come from HBM once and are
+// shared through LDS, where one-tile workgroups of the few-query kernel would each stream
+// them); 0: the few-query kernel.
+static inline int aw_group(int nqt) { return nqt >= 4 ? 4 : nqt >= 2 ? 2 : 0; }
 
+// Many-query kernel (one workgroup per CU): split the keys only when the workgroups fill less
+// than half of the 256 CUs.  A workgroup's time per key tile hardly changes with the number of
+// workgroups (measured: 768 queries x 32 heads, 192 workgroups, 79 us whole; 4 chunks 70 us
+// plus 21 us to merge), so splitting pays only when most CUs would idle.
 static inline void attn_wide_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk) {
-  const long wgs = (long)((attn_tiles(rs, H, Hkv) + AW_GROUP - 1) / AW_GROUP) * rs.B * Hkv;
+  const int nqt = attn_tiles(rs, H, Hkv), qg = aw_group(nqt);
+  const long wgs = (long)((nqt + qg - 1) / qg) * rs.B * Hkv;
   const int kt = (rs.L + 31) / 32;
   int want = wgs * 2 > 256 ? 1 : (int)std::min<long>(4, 256 / wgs);
   want = std::max(1, std::min(want, kt / 2));
@@ -66,11 +70,11 @@ static inline void attn_wide_plan(RowSet rs, int H, int Hkv, int &splits, int &c
 size_t attention_part_bytes(RowSet rs, int H, int Hkv, int hd, int dtype) {
   if (dtype == 0) return 0;
   int splits, chunk;
-  const int nqt = attn_tiles(rs, H, Hkv);
-  if (nqt >= AW_GROUP) {
+  const int nqt = attn_tiles(rs, H, Hkv), qg = aw_group(nqt);
+  if (qg) {
     attn_wide_plan(rs, H, Hkv, splits, chunk);
     if (splits == 1) return 0;
-    const int n_qt = (nqt + AW_GROUP - 1) / AW_GROUP * AW_GROUP;
+    const int n_qt = (nqt + qg - 1) / qg * qg;
     return (size_t)splits * rs.B * Hkv * n_qt * 32 * (hd + 2) * sizeof(float);
   }
   attn_plan(rs, H, Hkv, splits, chunk);
@@ -286,10 +290,11 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   }
 }
 
-// Many-query variant (block refresh): 8 waves per workgroup, all of the same (batch row, K/V
-// head): 4 query tiles of 32 queries, each run by two waves that take alternate 32-key tiles
-// (key half 0 the even ones, key half 1 the odd ones), so every SIMD holds two waves and one
-// wave's MFMAs overlap the other's softmax and LDS reads.  Each iteration brings one pair of
+// Many-query variant (block refresh, steps of wide blocks): 2 QT waves per workgroup, all of the
+// same (batch row, K/V head): QT query tiles of 32 queries (4, or 2 when a pair has only two or
+// three), each run by two waves that take alternate 32-key tiles (key half 0 the even ones,
+// key half 1 the odd ones); with QT = 4 every SIMD holds two waves and one wave's MFMAs overlap
+// the other's softmax and LDS reads.  Each iteration brings one pair of
 // key tiles (K and V^T, hi and lo) straight from global memory into one of two LDS slots
 // (global_load_lds, 16 bytes per lane, no register staging) while the waves work on the other
 // slot; one barrier per iteration.  At the end the two waves of a query tile merge their
@@ -298,14 +303,14 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 // (r >> 2) & 3 for 4), so the fragment reads of 16 consecutive rows cover the 64 banks (256
 // bytes) of the LDS once.  When the workgroups cannot fill the GPU the keys are split into chunks
 // (partials + the merge kernel).
-static constexpr int AW_WAVES = 4, AW_KH = 2;  // query tiles per workgroup, key halves
+static constexpr int AW_KH = 2;  // key halves
 
 __device__ inline int aw_swz(int r, int cpr) {
   return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-template <int HD>
-__global__ __launch_bounds__(64 * AW_WAVES * AW_KH, 1) void attn_wide_kernel(
+template <int HD, int QT>
+__global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
     RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part,
@@ -314,14 +319,14 @@ __global__ __launch_bounds__(64 * AW_WAVES * AW_KH, 1) void attn_wide_kernel(
   constexpr int PLANE = 32 * HD * 2;          // bytes of one plane of a 32-key tile
   constexpr int TILE = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
   constexpr int PAIR = AW_KH * TILE;          // the tiles of one iteration, one per key half
-  constexpr int NW = AW_WAVES * AW_KH;
+  constexpr int NW = QT * AW_KH;
   constexpr int LPW = PAIR / 1024 / NW;       // 1 KB loads per wave per iteration
   constexpr int KCPR = HD / 8, VCPR = 4;      // 16-byte chunks per K row / per V^T row
-  static_assert(PAIR % (1024 * NW) == 0 && LPW >= 1 && LPW <= 15, "tile staging");
-  static_assert(LPW * 64 * AW_WAVES == TILE / 16, "the waves of key half h load tile h");
+  static_assert(PAIR % (1024 * NW) == 0 && LPW >= 1 && LPW <= 32, "tile staging");
+  static_assert(LPW * 64 * QT == TILE / 16, "the waves of key half h load tile h");
   // the merge of the key halves reuses the ring: outputs [query tile][d][i][lane], then
   // (reference maximum, sum) [query tile][2][lane]
-  static_assert(AW_WAVES * (DB * 16 + 2) * 64 * 4 <= 2 * PAIR, "merge area");
+  static_assert(QT * (DB * 16 + 2) * 64 * 4 <= 2 * PAIR, "merge area");
   typedef __attribute__((address_space(3))) void lds_void;
   __shared__ __align__(1024) unsigned char lds[2 * PAIR];
 
@@ -331,11 +336,11 @@ __global__ __launch_bounds__(64 * AW_WAVES * AW_KH, 1) void attn_wide_kernel(
   int bg, grp;
   attn_grid_order(blockIdx.x, npairs, bg, grp);
   if (bg >= npairs) return;  // the whole workgroup, before any barrier
-  const int n_qt = gridDim.x / ((npairs + 7) / 8 * 8) * AW_WAVES;
+  const int n_qt = gridDim.x / ((npairs + 7) / 8 * 8) * QT;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int qw = wave % AW_WAVES, kh = wave / AW_WAVES;
-  const int qt = grp * AW_WAVES + qw;
+  const int qw = wave % QT, kh = wave / QT;
+  const int qt = grp * QT + qw;
   const int r = qt * 32 + col;
   const bool valid = r < nrows;
   const int pi = valid ? r / G : 0;
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(64 * AW_WAVES * AW_KH, 1) void attn_wide_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
   __syncthreads();
   float *xo = (float *)lds;
-  float *xm = xo + AW_WAVES * DB * 16 * 64;
+  float *xm = xo + QT * DB * 16 * 64;
   if (kh == 1) {
 #pragma unroll
     for (int d = 0; d < DB; ++d)
@@ -658,25 +663,27 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
   }
   const int nqt = attn_tiles(rs, H, Hkv);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
-  if (nqt >= AW_WAVES) {
-    // many queries: K/V tiles shared by the 4 waves of a workgroup through LDS
-    static_assert(AW_WAVES == AW_GROUP, "query tiles per workgroup");
+  const int qg = aw_group(nqt);
+  if (qg) {
+    // many queries: K/V tiles shared by the query tiles of a workgroup through LDS
     int wsplits, wchunk;
     attn_wide_plan(rs, H, Hkv, wsplits, wchunk);
-    const int groups = (nqt + AW_WAVES - 1) / AW_WAVES;
+    const int groups = (nqt + qg - 1) / qg;
     dim3 wgrid(attn_grid_x(rs.B * Hkv, groups), 1, wsplits);
+#define ATTNW_LAUNCH(HDV, QTV)                                                                   \
+  hipLaunchKernelGGL((attn_wide_kernel<HDV, QTV>), wgrid, dim3(64 * QTV * AW_KH), 0, st,         \
+                     (const bf16 *)q, (const bf16 *)q_lo, (const bf16 *)k_cache,                \
+                     (const bf16 *)k_cache_lo, (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, \
+                     rs, H, Hkv, wchunk, scale_log2, o_hi, o_lo, part, o_packed)
 #define ATTNW_CASE(HDV)                                                                          \
   case HDV:                                                                                      \
-    hipLaunchKernelGGL(attn_wide_kernel<HDV>, wgrid, dim3(64 * AW_WAVES * AW_KH), 0, st,          \
-                       (const bf16 *)q,                                                          \
-                       (const bf16 *)q_lo, (const bf16 *)k_cache, (const bf16 *)k_cache_lo,      \
-                       (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, rs, H, Hkv, wchunk,    \
-                       scale_log2, o_hi, o_lo, part, o_packed);                                  \
+    if (qg == 4) ATTNW_LAUNCH(HDV, 4);                                                           \
+    else ATTNW_LAUNCH(HDV, 2);                                                                   \
     if (wsplits > 1)                                                                             \
       hipLaunchKernelGGL(attn_merge_kernel<HDV>,                                                 \
-                         dim3((rs.B * Hkv * groups * AW_WAVES * 32 + MG_ROWS - 1) / MG_ROWS),    \
+                         dim3((rs.B * Hkv * groups * qg * 32 + MG_ROWS - 1) / MG_ROWS),          \
                          dim3(64 * MG_ROWS), 0, st, (const float *)part, rs, H, Hkv,             \
-                         groups * AW_WAVES, wsplits, o_hi, o_lo, o_packed);                      \
+                         groups * qg, wsplits, o_hi, o_lo, o_packed);                            \
     break;
     switch (hd) {
       ATTNW_CASE(32)
@@ -686,6 +693,7 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
         return hipErrorInvalidValue;
     }
 #undef ATTNW_CASE
+#undef ATTNW_LAUNCH
     return hipGetLastError();
   }
   int splits, chunk;
