@@ -462,9 +462,10 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Large-tile bf16 MFMA kernel for many rows (block refresh of long contexts and batches, and the
-// widest projections).  A workgroup of 8 waves (2 x 4, two per SIMD) owns a 256 x 256 tile; each
-// wave a 128 x 64 piece as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, so a W fragment read from
-// LDS feeds 8 MFMAs (4 blocks, hi and lo) and an A fragment 2.  K advances in stages of 32 through
+// widest projections).  A workgroup of 8 waves (4 x 2, two per SIMD) owns a 256 x 256 tile; each
+// wave a 64 x 128 piece as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16, so a W fragment read from
+// LDS feeds 4 MFMAs (2 blocks, hi and lo) and an A fragment 4: 8 fragment reads per 16 MFMAs,
+// where 128 x 64 pieces need 10 (A comes as hi and lo planes; measured ~0.5 % faster).  K advances in stages of 32 through
 // a ring of 3 LDS slots filled straight from global memory (global_load_lds, 16 bytes per lane,
 // no register staging), 2 stages ahead; one barrier per stage; the fragment reads of the next
 // 16-wide step go out before the MFMAs of the current one.  In a slot, a [rows][32] region holds
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 // conflict-free.  (Measured against a 4-wave version with 128 x 128 per wave: ~5 % faster, the
 // second wave per SIMD covers the barrier and fragment-read gaps.)
 static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NS = 3;
-static constexpr int BG_WGM = 2, BG_WGN = 4, BG_NT = 64 * BG_WGM * BG_WGN;  // waves, threads
+static constexpr int BG_WGM = 4, BG_WGN = 2, BG_NT = 64 * BG_WGM * BG_WGN;  // waves, threads
 static constexpr int BG_WM = BG_BM / BG_WGM / 32, BG_WN = BG_BN / BG_WGN / 32;  // blocks per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
   barrier();
   read_frags(0, 0, 0);
   for (int t = 0; t < T; ++t) {
-    // 2 BG_WM + BG_WN = 10 reads in flight at most (the LDS counter only counts to 15)
+    // 2 BG_WM + BG_WN = 8 reads in flight at most (the LDS counter only counts to 15)
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // buffer 0 is in registers
     read_frags(t, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
