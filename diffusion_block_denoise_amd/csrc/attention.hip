@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   // o[d][i]: dim d*32 + 8*(i/4) + 4*half + i%4 of query col
   if (gridDim.z == 1) {
     const float inv = 1.0f / lsum;
-    // output row m, columns head * HD + dim (panel-packed for a tiled output projection)
+    // output row m, columns head * HD + dim (panel-packed for a large-tile output projection)
     const size_t obase = o_packed ? pa_off(m, head * HD, ldq) : (size_t)m * ldq + head * HD;
     bf16 *oh = o_hi + obase;
     bf16 *ol = o_lo + obase;
