@@ -153,45 +153,74 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
     } break;
     case EPI_QKV: {
       const int hd = a.head_dim, half = hd / 2, H = a.n_heads, Hkv = a.n_kv_heads;
+      const int hs = __builtin_ctz(hd);  // head_dim is a power of two (launch_gemm checks)
       const int nq = H * hd, nk = Hkv * hd;
       const RowSet rs = a.rows;
-      // q and k columns, row-major (consecutive threads write consecutive dims)
+      // q and k columns, row-major: a thread keeps one column (consecutive threads write
+      // consecutive dims) and walks the rows NT / BN apart, its (batch row, slot) advancing with
+      // it, so nothing is divided per element
       if (n0 < nq + nk) {
-        for (int e = tid; e < BM * BN; e += NT) {
-          const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
-          if (m >= M || n >= a.N || n >= nq + nk) continue;
-          const int b = m / rs.nR, p = rs.start + m % rs.nR;
-          const int i = n % hd;
-          const float x = Ct[r * ldc + c];
+        static_assert(NT % BN == 0, "a thread keeps its column");
+        constexpr int RS = NT / BN;
+        const int c = tid % BN, n = n0 + c;
+        if (n < a.N && n < nq + nk) {
+          const int i = n & (hd - 1);
           const int j = i < half ? i : i - half;
-          const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angle of the slot's position
-          const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
-          const float y = i < half ? x * cs - Ct[r * ldc + c + half] * sn
-                                   : x * cs + Ct[r * ldc + c - half] * sn;
-          if (n < nq) {
-            store_val<T>(a.q_out, a.q_out_lo, (size_t)m * nq + n, y);
-          } else {
-            const int kvh = (n - nq) / hd;
-            store_val<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
+          const int pc = i < half ? c + half : c - half;  // the rotation partner (same head)
+          const bool is_q = n < nq;
+          const int kvh = (n - nq) >> hs;
+          int r = tid / BN, m = m0 + r;
+          int b = m / rs.nR, pr = m - b * rs.nR;
+          for (; r < BM && m < M; r += RS, m += RS) {
+            const int p = rs.start + pr;
+            const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angle of the slot's position
+            const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
+            const float x = Ct[r * ldc + c], xp = Ct[r * ldc + pc];
+            const float y = i < half ? x * cs - xp * sn : x * cs + xp * sn;
+            if (is_q)
+              store_val<T>(a.q_out, a.q_out_lo, (size_t)m * nq + n, y);
+            else
+              store_val<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
+            pr += RS;
+            while (pr >= rs.nR) { pr -= rs.nR; ++b; }
           }
         }
       }
       // v columns, row-fastest: consecutive threads write consecutive positions of one dim, which
-      // are adjacent in the transposed cache
+      // are adjacent in the transposed cache.  V^T per (batch row, K/V head): fp32 [hd][Lp]; bf16
+      // in 32-key tiles [Lp/32][hd][32], so that the attention's key tile is one contiguous run
+      // per plane, with the keys of a tile ordered as the attention's probability operand holds
+      // them (vt_key_pos)
       if (n0 + BN > nq + nk) {
-        for (int e = tid; e < BM * BN; e += NT) {
-          const int r = e % BM, c = e / BM, m = m0 + r, n = n0 + c;
-          if (m >= M || n >= a.N || n < nq + nk) continue;
-          const int b = m / rs.nR, p = rs.start + m % rs.nR;
-          const int i = n % hd;
-          const int kvh = (n - nq - nk) / hd;
-          // V^T per (batch row, K/V head): fp32 [hd][Lp]; bf16 in 32-key tiles [Lp/32][hd][32], so
-          // that the attention's key tile is one contiguous run per plane, with the keys of a tile
-          // ordered as the attention's probability operand holds them (vt_key_pos)
+        auto vt_index = [&](int b, int p, int kvh, int i) -> size_t {
           const size_t base = ((size_t)b * Hkv + kvh) * hd * rs.Lp;
-          const size_t vi = sizeof(T) == 2 ? base + (size_t)(p >> 5) * hd * 32 + i * 32 + vt_key_pos(p & 31)
-                                           : base + (size_t)i * rs.Lp + p;
-          store_val<T>(a.vt_cache, a.vt_cache_lo, vi, Ct[r * ldc + c]);
+          return sizeof(T) == 2 ? base + (size_t)(p >> 5) * hd * 32 + i * 32 + vt_key_pos(p & 31)
+                                : base + (size_t)i * rs.Lp + p;
+        };
+        if constexpr (NT % BM == 0) {
+          // a thread keeps one row and walks the columns NT / BM apart
+          constexpr int CS = NT / BM;
+          const int r = tid % BM, m = m0 + r;
+          if (m < M) {
+            const int b = m / rs.nR, p = rs.start + m % rs.nR;
+            for (int c = tid / BM; c < BN; c += CS) {
+              const int n = n0 + c;
+              if (n >= a.N) break;
+              if (n < nq + nk) continue;
+              const int t = n - nq - nk;
+              store_val<T>(a.vt_cache, a.vt_cache_lo, vt_index(b, p, t >> hs, t & (hd - 1)),
+                           Ct[r * ldc + c]);
+            }
+          }
+        } else {
+          for (int e = tid; e < BM * BN; e += NT) {
+            const int r = e % BM, c = e / BM, m = m0 + r, n = n0 + c;
+            if (m >= M || n >= a.N || n < nq + nk) continue;
+            const int t = n - nq - nk;
+            store_val<T>(a.vt_cache, a.vt_cache_lo,
+                         vt_index(m / rs.nR, rs.start + m % rs.nR, t >> hs, t & (hd - 1)),
+                         Ct[r * ldc + c]);
+          }
         }
       }
     } break;
@@ -1027,8 +1056,10 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
   GemmArgs a = a0;
   if (splits_out) *splits_out = 1;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  // panel-packed A only for the large-tile kernel; a packed SwiGLU output needs whole k blocks
-  if ((a.a_packed && !gemm_a_packed(a.M, a.N, a.K, dtype)) ||
+  // panel-packed A only for the large-tile kernel; a packed SwiGLU output needs whole k blocks;
+  // the q/k/v epilogue indexes heads with shifts
+  if ((a.epi == EPI_QKV && (a.head_dim <= 0 || (a.head_dim & (a.head_dim - 1)))) ||
+      (a.a_packed && !gemm_a_packed(a.M, a.N, a.K, dtype)) ||
       (a.epi == EPI_SWIGLU && a.act_packed && (dtype == 0 || a.ld_act % 32)))
     return hipErrorInvalidValue;
   hipError_t e;
