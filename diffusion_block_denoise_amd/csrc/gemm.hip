@@ -135,8 +135,8 @@ __device__ inline HeadAcc head_merge(HeadAcc a, HeadAcc b) {
 }
 
 template <typename T, int BM, int BN>
-__device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0, int n0) {
-  const int tid = threadIdx.x;
+__device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0, int n0,
+                             int tid) {  // tid: 0..NT-1 among the NT threads that run it
   const int M = a.M;
   switch (a.epi) {
     case EPI_STORE: {
@@ -286,10 +286,10 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
 // than the separate launch.
 template <int BM, int BN>
 __device__ void write_partial(const GemmArgs &a, int split, const float *Ct, int ldc, int m0,
-                              int n0) {
+                              int n0, int tid) {  // tid: 0..NT-1
   const int ld = a.N - a.n_tail0;
   float *P = a.partial + (size_t)split * a.M * ld - a.n_tail0;
-  for (int e = threadIdx.x; e < BM * BN; e += NT) {
+  for (int e = tid; e < BM * BN; e += NT) {
     const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
     if (m < a.M && n < a.N) P[(size_t)m * ld + n] = Ct[r * ldc + c];
   }
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int s
   }
   *(float4 *)(Ct + r * LDC + c) = s;
   __syncthreads();
-  run_epilogue<bf16, RD_BM, RD_BN>(a, Ct, LDC, m0, n0);
+  run_epilogue<bf16, RD_BM, RD_BN>(a, Ct, LDC, m0, n0, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -483,10 +483,10 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
       }
   __syncthreads();
   if (split >= 0) {
-    write_partial<BM, BN>(a, split, Ct, LDC, m0, n0);
+    write_partial<BM, BN>(a, split, Ct, LDC, m0, n0, tid);
     return;
   }
-  run_epilogue<bf16, BM, BN>(a, Ct, LDC, m0, n0);
+  run_epilogue<bf16, BM, BN>(a, Ct, LDC, m0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
   constexpr int IR = BG_BM * 4 / BG_NT;      // global_load_lds per wave and region: 2
   constexpr int VM_STAGE = 3 * IR;           // ... and per stage
   constexpr int LDC = 128 + 4;               // epilogue: 128 x 128 pieces of fp32
-  static_assert(128 * LDC * 4 <= BG_NS * STAGE, "epilogue tile must fit the ring");
+  static_assert(2 * 128 * LDC * 4 <= BG_NS * STAGE, "two epilogue pieces must fit the ring");
   static_assert(BG_BM == BG_BN && IR * BG_NT == BG_BM * 4, "one chunk per lane and load");
   __shared__ __align__(1024) unsigned char smem[BG_NS * STAGE];
   float *Ct = (float *)smem;
@@ -645,34 +645,35 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no load still writes the ring
   __syncthreads();
-  // Epilogue in 128 x 128 pieces: the waves whose 128 x 64 pieces lie in piece (h, q) write them
-  // into the C tile, then the first 256 threads run the epilogue on it.
-  constexpr int QR = BG_BM / BG_WGM, QC = BG_BN / BG_WGN;
+  // Epilogue in 128 x 128 pieces, the two of a 128-row half at a time: the waves whose 64 x 128
+  // pieces lie in half h write them into C tiles 0 and 1 (column half q = wn), then threads
+  // [q NT, (q + 1) NT) run the epilogue of piece (h, q), so every thread works.
+  static_assert(BG_BN == 2 * 128 && BG_NT == 2 * NT && BG_BN / BG_WGN == 128, "two pieces per half");
+  constexpr int QR = BG_BM / BG_WGM;
 #pragma unroll
-  for (int h = 0; h < BG_BM / 128; ++h)
+  for (int h = 0; h < BG_BM / 128; ++h) {
+    const int r0 = wm * QR - h * 128;
+    if (r0 >= 0 && r0 < 128) {
+      float *Cq = Ct + wn * (128 * LDC);
 #pragma unroll
-    for (int q = 0; q < BG_BN / 128; ++q) {
-      const int r0 = wm * QR - h * 128, c0 = wn * QC - q * 128;
-      if (r0 >= 0 && r0 < 128 && c0 >= 0 && c0 < 128) {
+      for (int i = 0; i < BG_WM; ++i)
 #pragma unroll
-        for (int i = 0; i < BG_WM; ++i)
+        for (int j = 0; j < BG_WN; ++j)
 #pragma unroll
-          for (int j = 0; j < BG_WN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = r0 + i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
-              Ct[row * LDC + c0 + j * 32 + frow] = acc[i][j][r];
-            }
-      }
-      __syncthreads();
-      if (tid < NT) {
-        if (split >= 0)
-          write_partial<128, 128>(a, split, Ct, LDC, m0 + h * 128, n0 + q * 128);
-        else
-          run_epilogue<bf16, 128, 128>(a, Ct, LDC, m0 + h * 128, n0 + q * 128);
-      }
-      __syncthreads();
+          for (int r = 0; r < 16; ++r) {
+            const int row = r0 + i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
+            Cq[row * LDC + j * 32 + frow] = acc[i][j][r];
+          }
     }
+    __syncthreads();
+    const int q = tid / NT, et = tid % NT;
+    const float *Cq = Ct + q * (128 * LDC);
+    if (split >= 0)
+      write_partial<128, 128>(a, split, Cq, LDC, m0 + h * 128, n0 + q * 128, et);
+    else
+      run_epilogue<bf16, 128, 128>(a, Cq, LDC, m0 + h * 128, n0 + q * 128, et);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -800,10 +801,10 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmArgs a) {
         Ct[(i * 16 + 4 * g + r) * LDC + wave * 32 + cb * 16 + rn] = acc[i][cb][r];
   __syncthreads();
   if (gridDim.z > 1) {
-    write_partial<BM, SK_BN>(a, blockIdx.z, Ct, LDC, 0, n0);
+    write_partial<BM, SK_BN>(a, blockIdx.z, Ct, LDC, 0, n0, tid);
     return;
   }
-  run_epilogue<bf16, BM, SK_BN>(a, Ct, LDC, 0, n0);
+  run_epilogue<bf16, BM, SK_BN>(a, Ct, LDC, 0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -842,7 +843,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const GemmArgs a) {
   for (int i = 0; i < 4; ++i)
     for (int j = 0; j < 4; ++j) Ct[(tr * 4 + i) * LDC + tc * 4 + j] = acc[i][j];
   __syncthreads();
-  run_epilogue<float, BM, BN>(a, Ct, LDC, m0, n0);
+  run_epilogue<float, BM, BN>(a, Ct, LDC, m0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------------------------
