@@ -146,6 +146,20 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
       }
     } break;
     case EPI_RESID: {
+      if (a.ld_out % 4 == 0 && a.N % 4 == 0) {
+        // 4 consecutive columns per access (the residual rows are 16-byte aligned)
+        constexpr int C4 = BN / 4;
+        for (int e = tid; e < BM * C4; e += NT) {
+          const int r = e / C4, c = (e % C4) * 4, m = m0 + r, n = n0 + c;
+          if (m >= M || n >= a.N) continue;
+          float4 *p = (float4 *)(a.resid + (size_t)m * a.ld_out + n);
+          const float4 x = *(const float4 *)(Ct + r * ldc + c);
+          float4 v = *p;
+          v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+          *p = v;
+        }
+        break;
+      }
       for (int e = tid; e < BM * BN; e += NT) {
         const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
         if (m < M && n < a.N) a.resid[(size_t)m * a.ld_out + n] += Ct[r * ldc + c];
@@ -289,6 +303,16 @@ __device__ void write_partial(const GemmArgs &a, int split, const float *Ct, int
                               int n0, int tid) {  // tid: 0..NT-1
   const int ld = a.N - a.n_tail0;
   float *P = a.partial + (size_t)split * a.M * ld - a.n_tail0;
+  if (ld % 4 == 0) {
+    // 4 consecutive columns per access (n0, ldc and, with ld, N are multiples of 4)
+    constexpr int C4 = BN / 4;
+    for (int e = tid; e < BM * C4; e += NT) {
+      const int r = e / C4, c = (e % C4) * 4, m = m0 + r, n = n0 + c;
+      if (m < a.M && n < a.N)
+        *(float4 *)(P + (size_t)m * ld + n) = *(const float4 *)(Ct + r * ldc + c);
+    }
+    return;
+  }
   for (int e = tid; e < BM * BN; e += NT) {
     const int r = e / BN, c = e % BN, m = m0 + r, n = n0 + c;
     if (m < a.M && n < a.N) P[(size_t)m * ld + n] = Ct[r * ldc + c];
