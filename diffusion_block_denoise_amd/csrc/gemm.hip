@@ -123,6 +123,26 @@ template <> __device__ inline void store_val<bf16>(void *p, void *p_lo, size_t i
   ((bf16 *)p_lo)[i] = lo;
 }
 
+// Store x[0..3] at elements i..i+3 (i a multiple of 4, the arrays 16-byte aligned): one fp32
+// 16-byte store, or one 8-byte store per bf16 plane.
+template <typename T> __device__ inline void store_val4(void *p, void *p_lo, size_t i, const float *x);
+template <> __device__ inline void store_val4<float>(void *p, void *, size_t i, const float *x) {
+  *(float4 *)((float *)p + i) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <> __device__ inline void store_val4<bf16>(void *p, void *p_lo, size_t i, const float *x) {
+  uint32_t hw[2], lw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bf16 h0, l0, h1, l1;
+    split_hilo(x[2 * j], h0, l0);
+    split_hilo(x[2 * j + 1], h1, l1);
+    hw[j] = (uint32_t)__bfloat16_as_ushort(h0) | ((uint32_t)__bfloat16_as_ushort(h1) << 16);
+    lw[j] = (uint32_t)__bfloat16_as_ushort(l0) | ((uint32_t)__bfloat16_as_ushort(l1) << 16);
+  }
+  *(uint2 *)((bf16 *)p + i) = make_uint2(hw[0], hw[1]);
+  *(uint2 *)((bf16 *)p_lo + i) = make_uint2(lw[0], lw[1]);
+}
+
 struct HeadAcc {
   float m1; int idx; float m2;
 };
@@ -170,31 +190,34 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
       const int hs = __builtin_ctz(hd);  // head_dim is a power of two (launch_gemm checks)
       const int nq = H * hd, nk = Hkv * hd;
       const RowSet rs = a.rows;
-      // q and k columns, row-major: a thread keeps one column (consecutive threads write
-      // consecutive dims) and walks the rows NT / BN apart, its (batch row, slot) advancing with
-      // it, so nothing is divided per element
+      // q and k columns, row-major: a thread keeps 4 consecutive columns of one head (one side of
+      // its rotation halves; consecutive threads write consecutive dims) and walks the rows
+      // NT / (BN / 4) apart, its (batch row, slot) advancing with it, so nothing is divided per
+      // element and every load and store moves 4 values
       if (n0 < nq + nk) {
-        static_assert(NT % BN == 0, "a thread keeps its column");
-        constexpr int RS = NT / BN;
-        const int c = tid % BN, n = n0 + c;
+        static_assert(NT % (BN / 4) == 0 && BN % 4 == 0, "a thread keeps its 4 columns");
+        constexpr int RS = NT / (BN / 4);
+        const int c = (tid % (BN / 4)) * 4, n = n0 + c;
         if (n < a.N && n < nq + nk) {
-          const int i = n & (hd - 1);
+          const int i = n & (hd - 1);               // i..i+3: one side of the halves (half % 4 == 0)
           const int j = i < half ? i : i - half;
-          const int pc = i < half ? c + half : c - half;  // the rotation partner (same head)
+          const int pc = i < half ? c + half : c - half;  // the rotation partners (same head)
+          const float sg = i < half ? -1.f : 1.f;
           const bool is_q = n < nq;
           const int kvh = (n - nq) >> hs;
-          int r = tid / BN, m = m0 + r;
+          int r = tid / (BN / 4), m = m0 + r;
           int b = m / rs.nR, pr = m - b * rs.nR;
           for (; r < BM && m < M; r += RS, m += RS) {
             const int p = rs.start + pr;
-            const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angle of the slot's position
-            const float cs = a.rope_cos[rp], sn = a.rope_sin[rp];
-            const float x = Ct[r * ldc + c], xp = Ct[r * ldc + pc];
-            const float y = i < half ? x * cs - xp * sn : x * cs + xp * sn;
+            const size_t rp = (size_t)rs.pos(p) * half + j;  // rotary angles of the slot's position
+            const float4 cs = *(const float4 *)(a.rope_cos + rp), sn = *(const float4 *)(a.rope_sin + rp);
+            const float4 x = *(const float4 *)(Ct + r * ldc + c), xp = *(const float4 *)(Ct + r * ldc + pc);
+            const float y[4] = {x.x * cs.x + sg * (xp.x * sn.x), x.y * cs.y + sg * (xp.y * sn.y),
+                                x.z * cs.z + sg * (xp.z * sn.z), x.w * cs.w + sg * (xp.w * sn.w)};
             if (is_q)
-              store_val<T>(a.q_out, a.q_out_lo, (size_t)m * nq + n, y);
+              store_val4<T>(a.q_out, a.q_out_lo, (size_t)m * nq + n, y);
             else
-              store_val<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
+              store_val4<T>(a.k_cache, a.k_cache_lo, (((size_t)b * Hkv + kvh) * rs.Lp + p) * hd + i, y);
             pr += RS;
             while (pr >= rs.nR) { pr -= rs.nR; ++b; }
           }
@@ -241,6 +264,21 @@ __device__ void run_epilogue(const GemmArgs &a, const float *Ct, int ldc, int m0
     case EPI_SWIGLU: {
       const int half = BN / 2;
       const int f0 = (n0 / BN) * half;
+      if (!a.act_f32 && a.ld_act % 4 == 0 && a.n_half % 4 == 0) {
+        // 4 consecutive outputs per thread (one 8-byte store per plane; f and ld_act are
+        // multiples of 4, so in the panel-packed layout too they are adjacent)
+        constexpr int H4 = BN / 8;
+        for (int e = tid; e < BM * H4; e += NT) {
+          const int r = e / H4, c = (e % H4) * 4, m = m0 + r, f = f0 + c;
+          if (m >= M || f >= a.n_half) continue;
+          const float4 g = *(const float4 *)(Ct + r * ldc + c);
+          const float4 u = *(const float4 *)(Ct + r * ldc + c + half);
+          const float y[4] = {silu_f(g.x) * u.x, silu_f(g.y) * u.y, silu_f(g.z) * u.z, silu_f(g.w) * u.w};
+          const size_t o = a.act_packed ? pa_off(m, f, a.ld_act) : (size_t)m * a.ld_act + f;
+          store_val4<bf16>(a.act_hi, a.act_lo, o, y);
+        }
+        break;
+      }
       for (int e = tid; e < BM * half; e += NT) {
         const int r = e / half, c = e % half, m = m0 + r, f = f0 + c;
         if (m >= M || f >= a.n_half) continue;
