@@ -371,12 +371,18 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(const GemmArgs a, int s
   const int r = threadIdx.x / (RD_BN / 4), c = (threadIdx.x % (RD_BN / 4)) * 4;
   const int m = m0 + r, n = n0 + c;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (m < a.M && n < a.N) {  // N is a multiple of 4 (widths are multiples of 64)
+  if (m < a.M && n + 3 < a.N && ld % 4 == 0) {  // whole, 16-byte aligned column groups
     const float *p = a.partial + (size_t)m * ld + (n - a.n_tail0);
     for (int z = 0; z < splits; ++z) {
       const float4 v = *(const float4 *)(p + z * MN);
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
+  } else if (m < a.M && n < a.N) {  // a width that is not a multiple of 4 (a vocabulary)
+    const float *p = a.partial + (size_t)m * ld + (n - a.n_tail0);
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z)
+      for (int q = 0; q < 4 && n + q < a.N; ++q) t[q] += p[z * MN + q];
+    s = make_float4(t[0], t[1], t[2], t[3]);
   }
   *(float4 *)(Ct + r * LDC + c) = s;
   __syncthreads();

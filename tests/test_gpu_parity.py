@@ -62,6 +62,7 @@ def test_tiny_f32_teacher_forced_all_blocks():
     dict(use_cache=0, head_dim=128, n_heads=2, n_kv_heads=1, batch=1),  # no cache, hd 128
     dict(batch=5, block_size=32, gen_length=64, prompt_len=17),  # M = 160 rows, ragged L
     dict(block_size=64, gen_length=64, batch=1, threshold=0.5),  # 64-wide block
+    dict(vocab=1001, mask_id=1000),  # vocabulary not a multiple of 4: ragged split-K partials
 ])
 def test_bf16_teacher_forced(variant):
     cfg = small_bf16(**variant)
