@@ -199,8 +199,8 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_h = take(Mmax * p.d * 4);
   // GEMM input a: RMSNorm(h) [Mmax][d] or the attention output [Mmax][nq]; bf16 hi/lo planes,
   // or fp32 in the hi slot
-  // (bf16 planes are panel-packed, 128-row panels, when their consumer GEMM is tiled: rows are
-  // allocated up to the next multiple of 128)
+  // (bf16 planes are panel-packed, 128-row panels, when their consumer GEMM runs on the
+  // large-tile kernel: rows are allocated up to the next multiple of 128)
   const size_t wa = std::max(p.d, p.nq), Mpad = (Mmax + 127) / 128 * 128;
   p.off_ahi = take(Mpad * wa * (p.dt ? 2 : 4));
   p.off_alo = take(p.dt ? Mpad * wa * 2 : 0);
@@ -369,7 +369,6 @@ void *q_lo(dllm_t *h) { return (char *)h->q + h->p.Mmax * h->p.nq * 2; }
 int a_packed(const dllm_t *h, int M, int N, int K) {
   return h->p.dt == 1 && gemm_a_packed(M, N, K, 1);
 }
-
 
 GemmArgs gemm_base(dllm_t *h, const void *a_hi, const void *a_lo, int lda, int M, int N, int K) {
   GemmArgs g;
