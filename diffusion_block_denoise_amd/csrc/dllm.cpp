@@ -13,9 +13,9 @@
 // back the per-row remaining-mask counts (one small copy per step).
 #include <hip/hip_runtime.h>
 
-#include <chrono>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -92,7 +92,7 @@ struct Plan {
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
-      off_ncom, off_rem, off_wpack, off_hc, off_qc, total;
+      off_cnt, off_wpack, off_hc, off_qc, total;
   // packed bf16 weights (elements): per layer QKV, Wo, gate/up, down, then the lm_head
   int n_gu;  // virtual gate/up width (64 gate + 64 up rows per 128-row panel)
   size_t wp_qkv, wp_o, wp_gu, wp_down, wp_layer, wp_lm;
@@ -214,8 +214,8 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_conf = take((size_t)p.B * p.Bs * 4);
   p.off_p2 = take((size_t)p.B * p.Bs * 4);
   p.off_com = take((size_t)p.B * p.Bs);
-  p.off_ncom = take((size_t)p.B * 4);
-  p.off_rem = take((size_t)p.B * 4);
+  // per batch row: committed, remaining masked and NaN-confidence counts of the last step
+  p.off_cnt = take((size_t)3 * p.B * 4);
   // the block rows' residual stream and queries in the last layer (forward)
   p.off_hc = take((size_t)p.B * p.Bs * p.d * 4);
   p.off_qc = take((size_t)p.B * p.Bs * p.nq * 4);
@@ -245,7 +245,7 @@ struct dllm_handle {
   int *tok;
   float *conf, *p2;
   uint8_t *com;
-  int *ncom, *rem;
+  int *cnt;  // [3][B]: committed, remaining masked, NaN confidences (last step)
   // decode state
   bool have_tokens = false;
   int block = -1, j = 0;
@@ -253,8 +253,13 @@ struct dllm_handle {
   bool any_forward = false;
   RowSet last_rows{};
   dllm_stats stats{};
-  std::vector<int> h_rem, h_ncom;
+  std::vector<int> h_cnt;
   std::string err;
+  // GPU time of the refreshes and steps: event pairs on the stream, read at the next
+  // synchronisation (dllm_block_begin is asynchronous)
+  hipEvent_t ev_ref[2] = {nullptr, nullptr}, ev_step[2] = {nullptr, nullptr};
+  bool ref_pending = false;
+  bool debug_sync = false;  // DLLM_DEBUG_SYNC: synchronise and check after every HIP call
   // per-kernel-class timing (dllm_set_profiling)
   struct Pending {
     int cls;
@@ -268,14 +273,19 @@ struct dllm_handle {
   dllm_kernel_prof prof[DLLM_KC_COUNT] = {};
   ~dllm_handle() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : {ev_ref[0], ev_ref[1], ev_step[0], ev_step[1]})
+      if (e) (void)hipEventDestroy(e);
   }
 };
 
 namespace {
 
+// With DLLM_DEBUG_SYNC set (h->debug_sync) every call is followed by a stream synchronisation,
+// so an asynchronous failure is reported by the call that caused it.
 #define HIPCHK(expr)                                                                     \
   do {                                                                                   \
     hipError_t e_ = (expr);                                                              \
+    if (e_ == hipSuccess && h->debug_sync) e_ = hipStreamSynchronize(h->st);             \
     if (e_ != hipSuccess) {                                                              \
       h->err = std::string(#expr) + ": " + hipGetErrorString(e_);                        \
       return DLLM_EHIP;                                                                  \
@@ -582,27 +592,42 @@ int hist_bin(int n) {
   return 8;
 }
 
-double now_ms() {
-  return std::chrono::duration<double, std::milli>(
-             std::chrono::steady_clock::now().time_since_epoch())
-      .count();
+// Book the GPU time of an enqueued refresh into the stats once its end event has completed
+// (wait: block until it has).
+int resolve_refresh_time(dllm_t *h, bool wait) {
+  if (!h->ref_pending) return DLLM_OK;
+  if (!wait) {
+    const hipError_t q = hipEventQuery(h->ev_ref[1]);
+    if (q == hipErrorNotReady) return DLLM_OK;
+    HIPCHK(q);
+  } else {
+    HIPCHK(hipEventSynchronize(h->ev_ref[1]));
+  }
+  float ms = 0.f;
+  HIPCHK(hipEventElapsedTime(&ms, h->ev_ref[0], h->ev_ref[1]));
+  h->stats.ms_refresh += ms;
+  h->ref_pending = false;
+  return DLLM_OK;
 }
 
 int do_block_begin(dllm_t *h, int b) {
-  const double t0 = now_ms();
+  int rc = resolve_refresh_time(h, true);  // the event pair is reused
+  if (rc) return rc;
   h->block = b;
   h->j = 0;
-  int rc = refresh(h);
+  HIPCHK(hipEventRecord(h->ev_ref[0], h->st));
+  rc = refresh(h);
   if (rc) return rc;
+  HIPCHK(hipEventRecord(h->ev_ref[1], h->st));
+  h->ref_pending = true;
   h->fresh = true;
-  h->stats.ms_refresh += now_ms() - t0;
   return DLLM_OK;
 }
 
 int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   const Plan &p = h->p;
-  const double t0 = now_ms();
   int rc;
+  HIPCHK(hipEventRecord(h->ev_step[0], h->st));
   if (!h->fresh) {
     const int s = p.P + h->block * p.Bs;
     if (h->cfg.use_cache == DLLM_NO_CACHE || h->cfg.refresh_every_step) {
@@ -622,25 +647,31 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   h->fresh = false;
   const int s = p.P + h->block * p.Bs;
   HIPCHK(launch_commit(h->x, p.L, p.B, s, p.Bs, h->tok, h->conf, h->cfg.threshold, floor_count(p, h->j),
-                       h->cfg.mask_id, h->com, h->ncom, h->rem, h->st));
-  HIPCHK(hipMemcpyAsync(h->h_ncom.data(), h->ncom, p.B * 4, hipMemcpyDeviceToHost, h->st));
-  HIPCHK(hipMemcpyAsync(h->h_rem.data(), h->rem, p.B * 4, hipMemcpyDeviceToHost, h->st));
+                       h->cfg.mask_id, h->com, h->cnt, h->cnt + p.B, h->cnt + 2 * p.B, h->st));
+  HIPCHK(hipEventRecord(h->ev_step[1], h->st));
+  HIPCHK(hipMemcpyAsync(h->h_cnt.data(), h->cnt, (size_t)3 * p.B * 4, hipMemcpyDeviceToHost, h->st));
   HIPCHK(hipStreamSynchronize(h->st));
   if (!h->pending.empty()) {
     int prc = prof_resolve(h);
     if (prc) return prc;
   }
+  rc = resolve_refresh_time(h, true);
+  if (rc) return rc;
+  float ms = 0.f;
+  HIPCHK(hipEventElapsedTime(&ms, h->ev_step[0], h->ev_step[1]));
+  h->stats.ms_step += ms;
   h->j++;
   h->stats.steps++;
   int done = 1;
   for (int b = 0; b < p.B; ++b) {
-    h->stats.committed += h->h_ncom[b];
-    h->stats.commits_hist[hist_bin(h->h_ncom[b])]++;
-    if (h->h_rem[b]) done = 0;
-    if (n_committed) n_committed[b] = h->h_ncom[b];
+    const int nc = h->h_cnt[b], rem = h->h_cnt[p.B + b], nan = h->h_cnt[2 * p.B + b];
+    h->stats.committed += nc;
+    h->stats.commits_hist[hist_bin(nc)]++;
+    h->stats.nan_count += nan;
+    if (rem) done = 0;
+    if (n_committed) n_committed[b] = nc;
   }
   if (block_done) *block_done = done;
-  h->stats.ms_step += now_ms() - t0;
   return DLLM_OK;
 }
 
@@ -711,9 +742,12 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->tok = (int *)(ws + p.off_tok);
   h->conf = (float *)(ws + p.off_conf); h->p2 = (float *)(ws + p.off_p2);
   h->com = (uint8_t *)(ws + p.off_com);
-  h->ncom = (int *)(ws + p.off_ncom); h->rem = (int *)(ws + p.off_rem);
-  h->h_rem.assign(p.B, 0);
-  h->h_ncom.assign(p.B, 0);
+  h->cnt = (int *)(ws + p.off_cnt);
+  h->h_cnt.assign((size_t)3 * p.B, 0);
+  {
+    const char *ds = getenv("DLLM_DEBUG_SYNC");
+    h->debug_sync = ds && *ds && strcmp(ds, "0") != 0;
+  }
   // Zero the K/V cache (its padding slots must hold zeros); rotary table.
   auto fail = [&](hipError_t e, const char *what) {
     g_create_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -721,6 +755,8 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
     return DLLM_EHIP;
   };
   hipError_t e;
+  for (hipEvent_t *ev : {&h->ev_ref[0], &h->ev_ref[1], &h->ev_step[0], &h->ev_step[1]})
+    if ((e = hipEventCreate(ev)) != hipSuccess) return fail(e, "event");
   if ((e = launch_fill_u32((uint32_t *)h->kc, 0, (p.off_cos - p.off_k) / 4, h->st)) != hipSuccess)
     return fail(e, "zero cache");
   if ((e = launch_rope_table(h->cos_t, h->sin_t, p.L, p.hd, cfg->rope_base, h->st)) != hipSuccess)
@@ -767,10 +803,13 @@ int dllm_prefill(dllm_t *h, const int32_t *prompt) {
                             hipMemcpyHostToDevice, h->st));
   HIPCHK(launch_init_tokens(h->x, p.B, p.P, p.L, h->cfg.mask_id, h->st));
   h->have_tokens = true;
-  int rc = do_block_begin(h, 0);
+  int rc = resolve_refresh_time(h, true);  // a refresh still in flight belongs to the old run
+  if (rc) return rc;
+  h->stats = dllm_stats{};
+  rc = do_block_begin(h, 0);
   if (rc) return rc;
   HIPCHK(hipStreamSynchronize(h->st));
-  return DLLM_OK;
+  return resolve_refresh_time(h, true);
 }
 
 int dllm_block_begin(dllm_t *h, int32_t block) {
@@ -788,8 +827,7 @@ int dllm_denoise_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
 
 int dllm_generate(dllm_t *h, const int32_t *prompt, int32_t *out, dllm_stats *stats) {
   if (!h) return DLLM_EINVAL;
-  h->stats = dllm_stats{};
-  int rc = dllm_prefill(h, prompt);
+  int rc = dllm_prefill(h, prompt);  // resets the counters
   if (rc) return rc;
   const int max_steps = h->p.G + h->p.NB;
   int steps = 0;
@@ -857,6 +895,8 @@ int dllm_debug_block_logits(dllm_t *h, float *logits_dev) {
 
 int dllm_get_stats(dllm_t *h, dllm_stats *stats) {
   if (!h || !stats) return DLLM_EINVAL;
+  int rc = resolve_refresh_time(h, true);
+  if (rc) return rc;
   *stats = h->stats;
   return DLLM_OK;
 }

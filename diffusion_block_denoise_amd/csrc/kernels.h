@@ -177,10 +177,11 @@ size_t attention_part_bytes(RowSet rows, int n_heads, int n_kv_heads, int head_d
 // Merge lm_head partials: tok, conf = 1/Z, p2 = exp(m2 - m1)/Z per row.
 hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,
                              float *p2, hipStream_t st);
-// Commit for each batch row over its block [s, s+Bs).
+// Commit for each batch row over its block [s, s+Bs); per row: positions committed, masked
+// positions left, and masked positions whose confidence is NaN.
 hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
                          float threshold, int k_floor, int mask_id, uint8_t *committed,
-                         int *n_committed, int *remaining, hipStream_t st);
+                         int *n_committed, int *remaining, int *n_nan, hipStream_t st);
 // x[b][p] = mask_id for P <= p < L (the prompt part is left as it is).
 hipError_t launch_init_tokens(int *x, int B, int P, int L, int mask_id, hipStream_t st);
 // cos/sin tables [L][hd/2] of theta = p * base^(-2i/hd), computed in fp64 on the device.

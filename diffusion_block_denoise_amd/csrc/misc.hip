@@ -206,22 +206,26 @@ hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int
 // ---------------------------------------------------------------------------------------------
 // Commit: one workgroup per batch row, thread i owns block position s + i.  A masked position
 // commits when conf > threshold or when fewer than k_floor masked positions rank above it
-// (confidence descending, then position ascending; NaN ranks last).
+// (confidence descending, then position ascending; NaN ranks last and is counted).
 __global__ __launch_bounds__(256) void commit_kernel(int *x, int L, int s, int Bs, const int *tok,
                                                      const float *conf, float threshold,
                                                      int k_floor, int mask_id, uint8_t *committed,
-                                                     int *n_committed, int *remaining) {
+                                                     int *n_committed, int *remaining, int *n_nan) {
   __shared__ float cs[256];
   __shared__ int ms[256];
-  __shared__ int cnt[2];
+  __shared__ int cnt[3];
   const int b = blockIdx.x, i = threadIdx.x;
-  if (i < 2) cnt[i] = 0;
+  if (i < 3) cnt[i] = 0;
+  __syncthreads();
   int masked = 0;
   float c = -INFINITY;
   if (i < Bs) {
     masked = x[(size_t)b * L + s + i] == mask_id;
     c = conf[(size_t)b * Bs + i];
-    if (c != c) c = -INFINITY;
+    if (c != c) {
+      c = -INFINITY;
+      if (masked) atomicAdd(&cnt[2], 1);
+    }
     cs[i] = c;
     ms[i] = masked;
   }
@@ -241,15 +245,16 @@ __global__ __launch_bounds__(256) void commit_kernel(int *x, int L, int s, int B
   if (i == 0) {
     n_committed[b] = cnt[0];
     remaining[b] = cnt[1];
+    n_nan[b] = cnt[2];
   }
 }
 
 hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
                          float threshold, int k_floor, int mask_id, uint8_t *committed,
-                         int *n_committed, int *remaining, hipStream_t st) {
+                         int *n_committed, int *remaining, int *n_nan, hipStream_t st) {
   if (Bs > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(256), 0, st, x, L, s, Bs, tok, conf, threshold,
-                     k_floor, mask_id, committed, n_committed, remaining);
+                     k_floor, mask_id, committed, n_committed, remaining, n_nan);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ class dllm_stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("full_forwards", C.c_int64),
                 ("cached_forwards", C.c_int64), ("committed", C.c_int64),
                 ("commits_hist", C.c_int64 * 9), ("ms_refresh", C.c_double),
-                ("ms_step", C.c_double)]
+                ("ms_step", C.c_double), ("nan_count", C.c_int64)]
 
     def as_dict(self) -> dict:
         d = {k: getattr(self, k) for k, _ in self._fields_}

@@ -26,6 +26,9 @@
  *     stream before returning; dllm_block_begin does not.
  *   - One host thread at a time per handle.  Several handles may share the
  *     same weights read-only.
+ *   - Environment: DLLM_DEBUG_SYNC=1 synchronises the stream after every HIP
+ *     call of the library, so an asynchronous failure is reported (as DLLM_EHIP)
+ *     by the call that caused it.
  *   - The library allocates no device memory: the caller passes the weights
  *     and one workspace of dllm_workspace_bytes() bytes, owns both, and must
  *     keep both alive until dllm_destroy.  The handle owns host state only.
@@ -125,7 +128,12 @@ typedef struct dllm_weights {
   const void *const *layer; /* host array of 9*n_layers device pointers */
 } dllm_weights;
 
-/* Counters of a handle since dllm_create (or the last dllm_prefill). */
+/*
+ * Counters of a handle since the last dllm_prefill (dllm_generate starts with one), or since
+ * dllm_create when there has been none.  The two times are GPU time on cfg.stream, measured with
+ * HIP events around the work each call enqueues: a refresh (dllm_block_begin is asynchronous) is
+ * booked once it has completed, at the next call that synchronises.
+ */
 typedef struct dllm_stats {
   int64_t steps;            /* denoising steps taken                         */
   int64_t full_forwards;    /* refresh / no-cache forwards                   */
@@ -134,8 +142,11 @@ typedef struct dllm_stats {
   int64_t commits_hist[9];  /* steps by tokens committed per row per step:
                                [0]=0, [1]=1, [2]=2, [3]=3-4, [4]=5-8, [5]=9-16,
                                [6]=17-32, [7]=33-64, [8]=65+                 */
-  double ms_refresh;        /* host wall time in block refreshes (ms)        */
-  double ms_step;           /* host wall time in denoise steps (ms)          */
+  double ms_refresh;        /* GPU time of the block refreshes (ms)          */
+  double ms_step;           /* GPU time of the denoise steps' own work (ms):
+                               cached forwards, statistics and commits       */
+  int64_t nan_count;        /* masked positions whose confidence was NaN
+                               (ranked last by the commit; should stay 0)    */
 } dllm_stats;
 
 typedef struct dllm_handle dllm_t;
@@ -162,10 +173,13 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
                 dllm_t **out);
 
 /*
- * x = [prompt | mask_id x gen_length] for every batch row, then the refresh of
- * block 0 (full forward over all positions, every cache slot written; its
- * block-row statistics serve the block's first step).  prompt: host int32
- * [batch, prompt_len], ids in [0, vocab).  Synchronises.
+ * Start of a decode: x = [prompt | mask_id x gen_length] for every batch row
+ * (the whole generated region starts masked: Fast-dLLM README, Quick Start,
+ * --gen_length), then the refresh of block 0 (full forward over all positions,
+ * every cache slot written; its block-row statistics serve the block's first
+ * step, "Fast-dLLM: Four Acceleration Tracks ...", section "The v1 Mechanism").
+ * Resets the dllm_stats counters.  prompt: host int32 [batch, prompt_len], ids
+ * in [0, vocab).  Synchronises.
  */
 int dllm_prefill(dllm_t *h, const int32_t *prompt);
 
@@ -179,12 +193,16 @@ int dllm_prefill(dllm_t *h, const int32_t *prompt);
 int dllm_block_begin(dllm_t *h, int32_t block);
 
 /*
- * One denoising step of the current block: the statistics (from the refresh on
- * the block's first step, otherwise from a cached forward: block rows for the
- * dual cache, block and later rows for the prefix cache, all rows with no
- * cache), then the commit: in every batch row, each masked block position
- * with confidence > threshold, plus at least the floor's number of most
- * confident ones (ties: lower position), gets its argmax token.
+ * One denoising step of the current block ("Fast-dLLM: Four Acceleration
+ * Tracks ...", section "The v1 Mechanism": confident positions are committed in
+ * parallel and never revised; section "Fast-dLLM v1 Versus a Standard Diffusion
+ * Sampler": the conventional schedule stays as the floor).  The statistics come
+ * from the refresh on the block's first step, otherwise from a cached forward:
+ * block rows for the dual cache, block and later rows for the prefix cache, all
+ * rows with no cache (Streaming-dLLM README tables, "Prefix-Cache" and
+ * "Fast-dLLM" columns).  Then the commit: in every batch row, each masked block
+ * position with confidence > threshold, plus at least the floor's number of
+ * most confident ones (ties: lower position), gets its argmax token.
  * n_committed: host int32 [batch] or NULL; block_done: host int32 or NULL,
  * set to 1 when no batch row has a masked position left in the block.
  * Synchronises (one small device-to-host copy).
@@ -192,9 +210,13 @@ int dllm_block_begin(dllm_t *h, int32_t block);
 int dllm_denoise_step(dllm_t *h, int32_t *n_committed, int32_t *block_done);
 
 /*
- * Whole decode: prefill, then every block in order (block_begin for b > 0,
- * steps until the block is done).  out: host int32 [batch, prompt_len +
- * gen_length] or NULL; stats: host or NULL (counters of this call).
+ * Whole decode (Fast-dLLM README, Quick Start: gen_length tokens in blocks of
+ * block_size, decoded left to right; ES-dLLM paper card, Streaming-dLLM
+ * abstract: block-wise diffusion): prefill, then every block in order
+ * (block_begin for b > 0, steps until the block is done).  out: host int32
+ * [batch, prompt_len + gen_length] or NULL; stats: host or NULL (counters of
+ * this call).  Fails with EINTERNAL if the steps exceed gen_length + the number
+ * of blocks (every step commits at least one position, so this never happens).
  */
 int dllm_generate(dllm_t *h, const int32_t *prompt, int32_t *out, dllm_stats *stats);
 
@@ -223,7 +245,7 @@ int dllm_get_step_info(dllm_t *h, int32_t *tok, float *conf, float *p2, uint8_t 
  */
 int dllm_debug_block_logits(dllm_t *h, float *logits_dev);
 
-/* Counters since dllm_create (dllm_generate resets them at its start). */
+/* Counters since the last dllm_prefill (see dllm_stats).  Waits for a refresh in flight. */
 int dllm_get_stats(dllm_t *h, dllm_stats *stats);
 
 /* Device-side phase of the handle for tests: current block, step index in it. */

@@ -39,8 +39,9 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu %zu\\n", sizeof(dllm_cfg), offsetof(dllm_cfg, threshold),
          offsetof(dllm_cfg, stream), sizeof(dllm_weights), sizeof(dllm_stats));
-  printf("%zu %zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
-         offsetof(dllm_cfg, suffix_window), offsetof(dllm_cfg, attention));
+  printf("%zu %zu %zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
+         offsetof(dllm_cfg, suffix_window), offsetof(dllm_cfg, attention),
+         offsetof(dllm_stats, nan_count));
   return 0;
 }}
 """)
@@ -51,7 +52,8 @@ int main(void) {{
     want = [C.sizeof(dllm.dllm_cfg), dllm.dllm_cfg.threshold.offset, dllm.dllm_cfg.stream.offset,
             C.sizeof(dllm.dllm_weights), C.sizeof(dllm.dllm_stats),
             dllm.dllm_stats.commits_hist.offset, dllm.dllm_stats.ms_step.offset,
-            dllm.dllm_cfg.suffix_window.offset, dllm.dllm_cfg.attention.offset]
+            dllm.dllm_cfg.suffix_window.offset, dllm.dllm_cfg.attention.offset,
+            dllm.dllm_stats.nan_count.offset]
     assert got == want
 
 

@@ -1,17 +1,24 @@
 """The GPU library at the full sizes of the benchmark workloads, in the launch configuration the
-benchmark uses.
+benchmark uses, teacher-forced against the oracle.
 
-* LLaDA-8B shape (batch 1, 768 positions, dual cache): one block teacher-forced against the
-  oracle for its refresh and two cached steps.
+* LLaDA-8B shape (batch 1, 768 positions, dual cache): blocks 0, 4 and 7 (the first, a middle
+  and the last block: the longest suffix and the longest prefix), the refresh and every cached
+  step until the block is committed.
 * Dream-7B shape (28/4 grouped heads, batch 8, 1536 positions): the GPU runs all 8 rows; the
-  oracle recomputes batch row 0 (rows are independent) for the refresh and one cached step.
-* Long-context LLaDA-8B shape (batch 16, 5120 positions, block 64): properties that hold at
-  any size (refresh determinism, batch-row permutation equivariance, commit invariants);
-  the oracle is too slow for a full forward there.
+  oracle follows batch rows 0 and 7 (rows are independent) at blocks 0, 8 and 15, for the
+  refresh and one cached step.
+* Long-context LLaDA-8B shape (batch 16, 5120 positions, block 64, the batch-16 refresh of
+  81920 rows, the 5120-key refresh attention, the 1024-row cached step):
+  - at the full 32-layer depth, batch row 15 at the last block: refresh and two cached steps;
+  - with the depth cut to 2 layers (the kernels and their plans depend on the row counts and
+    widths, not on the depth), batch rows 0 and 15 at the first and the last block;
+  - properties that hold at any size: refresh determinism, batch-row permutation, commits.
 
 The oracle's weights are the generator's values copied from the device tensors; a sample of
 every tensor is first checked against the host generator so that they are the same data.
 """
+
+import gc
 
 import numpy as np
 import pytest
@@ -26,6 +33,15 @@ def _log(*a):
     print(*a, flush=True)
 
 
+@pytest.fixture(autouse=True)
+def _free_device_memory():
+    """Each test holds tens of GB of weights and workspace: release them before the next."""
+    yield
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def _weights(cfg):
     import torch
     W = synth.weights_torch(cfg, device="cuda")
@@ -33,7 +49,7 @@ def _weights(cfg):
     return W
 
 
-def _host_weights_checked(cfg, W, rows=None):
+def _host_weights_checked(cfg, W):
     """fp32 host copies of the device weights, each spot-checked against the host generator."""
     names = synth.configs.weight_names(cfg["n_layers"])
     out = {}
@@ -52,58 +68,75 @@ def _host_weights_checked(cfg, W, rows=None):
     return out
 
 
-def _teacher_forced(cfg, h, dec, block, n_steps, rep, rows=None):
+def _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep):
+    """Refresh of `block` and up to n_steps steps (None: until the block is committed); the
+    oracle follows the batch rows `rows` of the GPU handle and feeds them its token state after
+    every step (the other rows run free on the GPU)."""
+    from oracle import decode as od
+    from oracle import model as om
+    rows = list(rows)
+    ocfg = dict(cfg, batch=len(rows))
+    dec = od.Decoder(om.Model(ocfg, Wh), keep_logits=True)
     x0 = synth.block_state_np(cfg, block)
-    dec.set_tokens(x0[:dec.B])
+    dec.set_tokens(x0[rows])
     h.set_tokens(x0)
     dec.block_begin(block)
     h.block_begin(block)
-    for j in range(n_steps):
+    j = 0
+    while True:
         x_before = dec.x.copy()
         rec, done = dec.step()
         h.denoise_step()
-        info = h.get_step_info()
-        info = {k: v[:dec.B] for k, v in info.items()}
-        lg = h.debug_block_logits()[:dec.B].cpu().numpy()
-        ocfg = dict(cfg, batch=dec.B)
+        info = {k: v[rows] for k, v in h.get_step_info().items()}
+        lg = h.debug_block_logits()[rows].cpu().numpy()
         compare_step(ocfg, rec, x_before, info, lg, rep)
-        _log(f"block {block} step {j}: {rep}")
+        _log(f"rows {rows} block {block} step {j}: {rep}")
         xg = h.get_tokens()
-        xg[:dec.B] = dec.x
+        xg[rows] = dec.x
         h.set_tokens(xg)
-        if done:
+        j += 1
+        if done or (n_steps is not None and j >= n_steps):
             break
 
 
-def test_llada8b_teacher_forced_block():
+def _run(cfg, cases):
+    """cases: (rows, block, n_steps) each; one handle, one report."""
     from diffusion_block_denoise_amd import dllm
-    from oracle import decode as od
-    from oracle import model as om
-    cfg = synth.configs.get("llada8b")
-    _log("case llada8b: weights")
+    _log(f"case {cfg['name']} ({cfg['n_layers']} layers): weights")
     W = _weights(cfg)
     h = dllm.Handle(cfg, W)
     Wh = _host_weights_checked(cfg, W)
-    dec = od.Decoder(om.Model(cfg, Wh), keep_logits=True)
     rep = Report()
-    _teacher_forced(cfg, h, dec, 3, 3, rep)
+    for rows, block, n_steps in cases:
+        _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep)
+    h.destroy()
+    return rep
+
+
+def test_llada8b_first_middle_last_blocks():
+    cfg = synth.configs.get("llada8b")
+    rep = _run(cfg, [((0,), 0, None), ((0,), 4, None), ((0,), 7, None)])
     assert_report(cfg, rep)
 
 
-def test_dream7b_teacher_forced_row0():
-    from diffusion_block_denoise_amd import dllm
-    from oracle import decode as od
-    from oracle import model as om
+def test_dream7b_rows_0_and_7():
     cfg = synth.configs.get("dream7b")
-    _log("case dream7b: weights")
-    W = _weights(cfg)
-    h = dllm.Handle(cfg, W)
-    Wh = _host_weights_checked(cfg, W)
-    ocfg = dict(cfg, batch=1)
-    dec = od.Decoder(om.Model(ocfg, Wh), keep_logits=True)
-    rep = Report()
-    _teacher_forced(cfg, h, dec, 5, 2, rep)
-    assert_report(ocfg, rep)
+    rep = _run(cfg, [((0, 7), 0, 2), ((0, 7), 8, 2), ((0, 7), 15, 2)])
+    assert_report(dict(cfg, batch=2), rep)
+
+
+def test_long_context_full_depth_last_block():
+    cfg = synth.configs.get("llada8b_long")
+    nb = cfg["gen_length"] // cfg["block_size"]
+    rep = _run(cfg, [((15,), nb - 1, 3)])
+    assert_report(dict(cfg, batch=1), rep)
+
+
+def test_long_context_two_layers_rows_0_and_15():
+    cfg = synth.configs.get("llada8b_long", n_layers=2)
+    nb = cfg["gen_length"] // cfg["block_size"]
+    rep = _run(cfg, [((0, 15), 0, 3), ((0, 15), nb - 1, 3)])
+    assert_report(dict(cfg, batch=2), rep)
 
 
 def test_long_context_properties():
@@ -148,3 +181,5 @@ def test_long_context_properties():
         prev = x
         if done:
             break
+    assert h.get_stats()["nan_count"] == 0
+    h.destroy()

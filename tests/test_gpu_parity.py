@@ -232,3 +232,60 @@ def test_profiling_counts_launches():
         assert prof[k]["ms"] > 0 and prof[k]["bytes"] > 0 and prof[k]["flops"] > 0
     h.set_profiling(0)
     assert h.get_profile()["attention"]["launches"] == 0
+
+
+# ------------------------------------------------------------------------------ resume
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16"])
+def test_resume_after_destroy_is_identical(name):
+    """Checkpoint / resume: the decode state is the token state plus the block index, and the
+    cache is a function of the token state at a block start.  A run stopped after two blocks,
+    its handle destroyed, and resumed on a new handle from dllm_set_tokens + dllm_block_begin
+    ends with the same tokens as an uninterrupted run."""
+    cfg = synth.configs.get("tiny_f32") if name == "tiny_f32" else small_bf16(
+        batch=3, gen_length=64, block_size=16, threshold=0.7)
+    prompt = synth.prompt_np(cfg)
+    nb = cfg["gen_length"] // cfg["block_size"]
+    h = _handle(cfg)
+    x_full, st_full = h.generate(prompt)
+    h.destroy()
+
+    def run_blocks(hh, blocks, begun):
+        """Steps through `blocks`; the first one's refresh has already run (`begun`)."""
+        steps = 0
+        for i, b in enumerate(blocks):
+            if i or not begun:
+                hh.block_begin(b)
+            done = False
+            while not done:
+                _, done = hh.denoise_step()
+                steps += 1
+        return steps
+
+    h1 = _handle(cfg)
+    h1.prefill(prompt)
+    s1 = run_blocks(h1, [0, 1], begun=True)
+    x_mid = h1.get_tokens()
+    assert h1.get_position()[0] == 1
+    h1.destroy()
+    h2 = _handle(cfg)
+    h2.set_tokens(x_mid)
+    h2.block_begin(2)
+    assert h2.get_position() == (2, 0)
+    s2 = run_blocks(h2, list(range(2, nb)), begun=True)
+    assert np.array_equal(h2.get_tokens(), x_full)
+    assert s1 + s2 == st_full["steps"]
+    assert h2.get_stats()["nan_count"] == 0
+
+
+def test_stats_reset_by_prefill_and_gpu_times():
+    """dllm_prefill resets the counters; the phase times are GPU times that add up."""
+    cfg = small_bf16(batch=2, gen_length=64, block_size=16)
+    h = _handle(cfg)
+    _, st = h.generate(synth.prompt_np(cfg))
+    h.prefill(synth.prompt_np(cfg))
+    st2 = h.get_stats()
+    assert st2["steps"] == 0 and st2["committed"] == 0 and st2["full_forwards"] == 1
+    assert st2["ms_refresh"] > 0 and st2["ms_step"] == 0
+    nb = cfg["gen_length"] // cfg["block_size"]
+    assert st["full_forwards"] == nb and st["ms_refresh"] > 0 and st["ms_step"] > 0
+    assert st["nan_count"] == 0
