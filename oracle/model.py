@@ -137,11 +137,14 @@ class Model:
 
     ``weights`` holds the storage-rounded values (fp32 arrays are fine: they are
     widened to fp64 at use).  Names follow ``synth.configs.weight_names``.
+    ``progress`` (optional) is called with (layer, n_layers, rows) after each layer of a
+    forward; it only reports, it takes no part in the arithmetic.
     """
 
-    def __init__(self, cfg: dict, weights):
+    def __init__(self, cfg: dict, weights, progress=None):
         self.cfg = cfg
         self.w = weights
+        self.progress = progress
         self.d = cfg["d_model"]
         self.H = cfg["n_heads"]
         self.Hkv = cfg["n_kv_heads"]
@@ -206,6 +209,8 @@ class Model:
             f = rms_norm(h, self._W(p + "ffn_norm"), eps)
             h = h + swiglu_ffn(f, self._W(p + "w_gate"), self._W(p + "w_up"),
                                self._W(p + "w_down"))
+            if self.progress is not None:
+                self.progress(l, cfg["n_layers"], n)
         return h
 
     def stats(self, hidden: np.ndarray) -> dict:

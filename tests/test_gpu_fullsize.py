@@ -65,6 +65,8 @@ def _host_weights_checked(cfg, W):
                         .astype(np.int64)]
             assert np.array_equal(flat[start:start + cnt], ref), n
         out[n] = t
+        if tid % 36 == 35:
+            _log(f"  host weights: {tid + 1}/{len(names)} tensors copied and checked")
     return out
 
 
@@ -76,7 +78,12 @@ def _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep):
     from oracle import model as om
     rows = list(rows)
     ocfg = dict(cfg, batch=len(rows))
-    dec = od.Decoder(om.Model(ocfg, Wh), keep_logits=True)
+
+    def progress(layer, n_layers, n_rows):
+        if n_rows > 256 and (layer % 4 == 3 or layer == n_layers - 1):
+            _log(f"  oracle forward over {n_rows} rows: layer {layer + 1}/{n_layers}")
+
+    dec = od.Decoder(om.Model(ocfg, Wh, progress=progress), keep_logits=True)
     x0 = synth.block_state_np(cfg, block)
     dec.set_tokens(x0[rows])
     h.set_tokens(x0)
