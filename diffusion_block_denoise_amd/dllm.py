@@ -105,6 +105,11 @@ def load(path: str | None = None):
     if not os.path.exists(p):
         raise RuntimeError(f"{p} not found: build the HIP library first "
                            "(python -m diffusion_block_denoise_amd.build)")
+    # torch first: its HIP runtime (torch/lib/libamdhip64.so, soname libamdhip64.so.7) is then the
+    # one the library's libamdhip64.so.7 dependency binds to.  Loaded the other way round, ROCm's
+    # copy comes in first and torch, which asks for the unversioned name, loads its own: two HIP
+    # runtimes in one process, and the second to touch the GPU finds no device.
+    import torch  # noqa: F401
     lib = C.CDLL(p)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
