@@ -22,7 +22,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              # no packed fp32 instructions in any kernel
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
-SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "dllm.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "scratch.hip", "dllm.cpp"]
 
 
 def hipcc() -> str:

@@ -27,6 +27,8 @@
 
 using namespace dllm;
 
+static_assert(STATIC_SCRATCH_BYTES == DLLM_STATIC_SCRATCH_BYTES, "static scratch size");
+
 namespace {
 
 std::string g_create_error;
@@ -93,6 +95,10 @@ struct Plan {
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
       off_cnt, off_wpack, off_hc, off_qc, total;
+  // The scratch region [off_scratch, total): partial results that live only within one launch
+  // sequence (split-K tiles, attention key-chunk partials, lm_head tile partials).  The
+  // static-scratch variant takes it from the library's static device array instead.
+  size_t off_scratch;
   // packed bf16 weights (elements): per layer QKV, Wo, gate/up, down, then the lm_head
   int n_gu;  // virtual gate/up width (64 gate + 64 up rows per 128-row panel)
   size_t wp_qkv, wp_o, wp_gu, wp_down, wp_layer, wp_lm;
@@ -207,9 +213,6 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_acthi = take(Mpad * p.F * (p.dt ? 2 : 4));
   p.off_actlo = take(p.dt ? Mpad * p.F * 2 : 0);
   p.off_q = take(Mmax * p.nq * 4);  // fp32, or bf16 hi plane + lo plane
-  p.off_apart = take(apart);
-  p.off_gpart = take(gpart);
-  p.off_hpart = take((size_t)p.B * p.Bs * p.n_vtiles * sizeof(HeadPart));
   p.off_tok = take((size_t)p.B * p.Bs * 4);
   p.off_conf = take((size_t)p.B * p.Bs * 4);
   p.off_p2 = take((size_t)p.B * p.Bs * 4);
@@ -219,6 +222,11 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   // the block rows' residual stream and queries in the last layer (forward)
   p.off_hc = take((size_t)p.B * p.Bs * p.d * 4);
   p.off_qc = take((size_t)p.B * p.Bs * p.nq * 4);
+  // scratch region last, so that a workspace without it is a prefix of the full one
+  p.off_scratch = o;
+  p.off_apart = take(apart);
+  p.off_gpart = take(gpart);
+  p.off_hpart = take((size_t)p.B * p.Bs * p.n_vtiles * sizeof(HeadPart));
   p.total = o;
 }
 
@@ -696,8 +704,14 @@ int dllm_workspace_bytes(const dllm_cfg *cfg, size_t *bytes) {
   return DLLM_OK;
 }
 
-int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
-                dllm_t **out) {
+}  // extern "C"
+
+namespace {
+
+// dllm_create and its static-scratch variant: `scratch` is NULL (the scratch region is the end
+// of the workspace) or the device address of the library's static array.
+int create_handle(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
+                  char *scratch, dllm_t **out) {
   if (!out) { g_create_error = "out is NULL"; return DLLM_EINVAL; }
   *out = nullptr;
   std::string m;
@@ -713,8 +727,9 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   if ((uintptr_t)workspace % ALIGN) { g_create_error = "workspace must be 256-byte aligned"; return DLLM_EINVAL; }
   Plan p;
   make_plan(cfg, p);
-  if (ws_bytes < p.total) {
-    g_create_error = "workspace too small: need " + std::to_string(p.total) + " bytes";
+  const size_t need = scratch ? p.off_scratch : p.total;
+  if (ws_bytes < need) {
+    g_create_error = "workspace too small: need " + std::to_string(need) + " bytes";
     return DLLM_ENOSPACE;
   }
   dllm_t *h = new (std::nothrow) dllm_handle();
@@ -736,9 +751,11 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   h->a_hi = ws + p.off_ahi; h->a_lo = ws + p.off_alo;
   h->act_hi = ws + p.off_acthi; h->act_lo = ws + p.off_actlo;
   h->q = ws + p.off_q;
-  h->apart = (float *)(ws + p.off_apart);
-  h->gpart = (float *)(ws + p.off_gpart);
-  h->hpart = (HeadPart *)(ws + p.off_hpart);
+  // scratch region: the end of the workspace, or the static array at the same relative offsets
+  char *sc = scratch ? scratch - p.off_scratch : ws;
+  h->apart = (float *)(sc + p.off_apart);
+  h->gpart = (float *)(sc + p.off_gpart);
+  h->hpart = (HeadPart *)(sc + p.off_hpart);
   h->tok = (int *)(ws + p.off_tok);
   h->conf = (float *)(ws + p.off_conf); h->p2 = (float *)(ws + p.off_p2);
   h->com = (uint8_t *)(ws + p.off_com);
@@ -790,6 +807,43 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
   if ((e = hipStreamSynchronize(h->st)) != hipSuccess) return fail(e, "synchronize");
   *out = h;
   return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, size_t ws_bytes,
+                dllm_t **out) {
+  return create_handle(w, cfg, workspace, ws_bytes, nullptr, out);
+}
+
+int dllm_create_static_scratch(const dllm_weights *w, const dllm_cfg *cfg, void *workspace,
+                               size_t *ws_bytes, dllm_t **out) {
+  if (!ws_bytes) { g_create_error = "ws_bytes is NULL"; return DLLM_EINVAL; }
+  std::string m;
+  int rc = check_cfg(cfg, m);
+  if (rc) { g_create_error = m; return rc; }
+  Plan p;
+  make_plan(cfg, p);
+  const size_t sbytes = p.total - p.off_scratch;
+  if (sbytes > STATIC_SCRATCH_BYTES) {
+    g_create_error = "static scratch too small for this configuration: need " +
+                     std::to_string(sbytes) + " bytes, the array holds " +
+                     std::to_string((size_t)STATIC_SCRATCH_BYTES);
+    return DLLM_ENOSPACE;
+  }
+  if (!workspace) {  // size query (host only)
+    *ws_bytes = p.off_scratch;
+    return DLLM_OK;
+  }
+  void *sp = nullptr;
+  const hipError_t e = static_scratch_address(&sp);
+  if (e != hipSuccess) {
+    g_create_error = std::string("static scratch address: ") + hipGetErrorString(e);
+    return DLLM_EHIP;
+  }
+  return create_handle(w, cfg, workspace, *ws_bytes, (char *)sp, out);
 }
 
 int dllm_prefill(dllm_t *h, const int32_t *prompt) {

@@ -191,6 +191,11 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t st);
 // a multiple of 16; src and dst must not overlap).
 hipError_t launch_gather_rows(const void *src, void *dst, int B, int n, int src_stride,
                               int src_off, size_t row_bytes, hipStream_t st);
+// Static device scratch (scratch.hip): the bytes of the file-scope array, and the device address
+// of the current device's copy (looked up once per device).
+static constexpr size_t STATIC_SCRATCH_BYTES = (size_t)256 << 20;
+hipError_t static_scratch_address(void **ptr);
+
 // Mark the mask id column (-inf) of debug logits rows.
 hipError_t launch_mask_column(float *logits, int n_rows, int vocab, int mask_id, hipStream_t st);
 

@@ -75,6 +75,8 @@ _SIGS = {
     "dllm_workspace_bytes": (C.c_int, [C.POINTER(dllm_cfg), C.POINTER(C.c_size_t)]),
     "dllm_create": (C.c_int, [C.POINTER(dllm_weights), C.POINTER(dllm_cfg), _P, C.c_size_t,
                               C.POINTER(_P)]),
+    "dllm_create_static_scratch": (C.c_int, [C.POINTER(dllm_weights), C.POINTER(dllm_cfg), _P,
+                                             C.POINTER(C.c_size_t), C.POINTER(_P)]),
     "dllm_prefill": (C.c_int, [_P, _I32P]),
     "dllm_block_begin": (C.c_int, [_P, C.c_int32]),
     "dllm_denoise_step": (C.c_int, [_P, _I32P, _I32P]),
@@ -154,14 +156,26 @@ def dllm_workspace_bytes(cfg: dllm_cfg) -> int:
     return n.value
 
 
+def static_scratch_workspace_bytes(cfg: dllm_cfg) -> int:
+    """Workspace bytes of a static-scratch handle (dllm_create_static_scratch's size query)."""
+    lib = load()
+    n = C.c_size_t(0)
+    rc = lib.dllm_create_static_scratch(None, C.byref(cfg), None, C.byref(n), None)
+    if rc:
+        raise DllmError("dllm_create_static_scratch", rc, lib.dllm_last_error(None).decode())
+    return n.value
+
+
 class Handle:
     """A dllm_t with the torch tensors it points at (weights, workspace) kept alive.
 
     Methods mirror the C functions (``dllm_`` prefix dropped) and only marshal arguments.
+    ``static_scratch``: create it with dllm_create_static_scratch (scratch in the library's
+    static device array, a smaller workspace).
     """
 
     def __init__(self, cfg: dict, weights: dict, stream=None, refresh_every_step=False,
-                 workspace=None):
+                 workspace=None, static_scratch=False):
         import torch
         self.lib = load()
         self.cfg = cfg
@@ -172,7 +186,8 @@ class Handle:
         rc = self.lib.dllm_validate_cfg(C.byref(self.c))
         if rc:
             raise DllmError("dllm_validate_cfg", rc, "invalid configuration")
-        self.ws_bytes = dllm_workspace_bytes(self.c)
+        self.ws_bytes = (static_scratch_workspace_bytes(self.c) if static_scratch
+                         else dllm_workspace_bytes(self.c))
         if workspace is None:
             workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device="cuda")
         self.workspace = workspace
@@ -190,10 +205,18 @@ class Handle:
                               weights["lm_head"].data_ptr(),
                               C.cast(self._layer, C.POINTER(C.c_void_p)))
         h = C.c_void_p()
-        rc = self.lib.dllm_create(C.byref(self.w), C.byref(self.c), C.c_void_p(aligned),
-                                  C.c_size_t(workspace.numel() - (aligned - base)), C.byref(h))
+        avail = workspace.numel() - (aligned - base)
+        if static_scratch:
+            n = C.c_size_t(avail)
+            rc = self.lib.dllm_create_static_scratch(C.byref(self.w), C.byref(self.c),
+                                                     C.c_void_p(aligned), C.byref(n), C.byref(h))
+            fn = "dllm_create_static_scratch"
+        else:
+            rc = self.lib.dllm_create(C.byref(self.w), C.byref(self.c), C.c_void_p(aligned),
+                                      C.c_size_t(avail), C.byref(h))
+            fn = "dllm_create"
         if rc:
-            raise DllmError("dllm_create", rc, self.lib.dllm_last_error(None).decode())
+            raise DllmError(fn, rc, self.lib.dllm_last_error(None).decode())
         self.h = h
         self.B = cfg["batch"]
         self.L = cfg["prompt_len"] + cfg["gen_length"]

@@ -173,6 +173,27 @@ int dllm_create(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, siz
                 dllm_t **out);
 
 /*
+ * For callers that cannot allocate device memory while they run (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same handle as dllm_create, except
+ * that its scratch (split-K partial tiles, attention key-chunk partials, lm_head tile partials:
+ * values that live only within one call's launches) is a static device array of the library,
+ * DLLM_STATIC_SCRATCH_BYTES bytes on each GPU it runs on, held until the process ends, and no
+ * longer part of the workspace.  The function itself allocates nothing.
+ *   - workspace == NULL: host-only size query; *ws_bytes receives the workspace bytes this
+ *     variant needs (dllm_workspace_bytes(cfg) less the scratch region).  w and out unused.
+ *   - otherwise: as dllm_create with *ws_bytes as the workspace size.  The scratch address is
+ *     that of the device current at this call; every call on the handle must run there.
+ *   - DLLM_ENOSPACE (query or create) when cfg's scratch exceeds DLLM_STATIC_SCRATCH_BYTES;
+ *     DLLM_EINVAL when ws_bytes is NULL or as for dllm_create.
+ * All handles of this kind on one GPU share the array, which keeps whatever the last call wrote
+ * (nothing in it needs to start at zero): calls on two such handles must not overlap in time
+ * (different streams or host threads race).  Handles made by dllm_create are unaffected.
+ */
+#define DLLM_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+int dllm_create_static_scratch(const dllm_weights *w, const dllm_cfg *cfg, void *workspace,
+                               size_t *ws_bytes, dllm_t **out);
+
+/*
  * Start of a decode: x = [prompt | mask_id x gen_length] for every batch row
  * (the whole generated region starts masked: Fast-dLLM README, Quick Start,
  * --gen_length), then the refresh of block 0 (full forward over all positions,
