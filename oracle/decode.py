@@ -44,6 +44,25 @@ What it follows
   only block b-1 (its tokens are now final; for b = 0 the prompt) and block b,
   and every later step recomputes block b.  Suffix pruning does not apply
   (nothing after the block is visible).
+* Early exit for converged tokens (``exit_steps`` N > 0, ``exit_floor`` c;
+  ES-dLLM paper card, Streaming-dLLM abstract: a dynamic confidence-aware
+  strategy with an early exit mechanism that skips the iterations of converged
+  tokens).  A masked position's run is the number of consecutive steps of the
+  current block, ending at this one, in which its argmax token stayed the same
+  and its confidence was above c (a step whose token differs from the previous
+  one starts a new run of 1; a confidence of c or less ends the run at 0).
+  After the step's commit rule, if every position of the row that is still
+  masked has a run of at least N, they are all committed with their argmax:
+  the row's block exits early.  N = 0 turns it off.
+* First-step confidence scheduling (``first_threshold`` t1 >= 0; ES-dLLM paper
+  card, CAI-DLLM abstract: first-step confidence commits easy tokens earlier,
+  gives the harder ones more denoising steps and adjusts the schedule per
+  output block).  The first step of a block commits with threshold t1 instead
+  of the threshold: the easy tokens go at once.  The positions of the row still
+  masked after it are the hard ones; the block's remaining spb - 1 steps of
+  the step budget are spread over them, so the floor of step j >= 1 is the
+  share of the hard positions for step j - 1 of spb - 1 steps (at least 1).
+  Each block, and each batch row, gets its own schedule.  t1 < 0 turns it off.
 """
 
 from __future__ import annotations
@@ -52,7 +71,8 @@ import numpy as np
 
 from .model import Model
 
-__all__ = ["steps_per_block", "floor_count", "commit_set", "Decoder"]
+__all__ = ["steps_per_block", "floor_count", "commit_set", "run_update", "hard_floor",
+           "Decoder"]
 
 NO_CACHE, PREFIX_CACHE, DUAL_CACHE = 0, 1, 2
 
@@ -93,6 +113,34 @@ def commit_set(masked: np.ndarray, conf: np.ndarray, threshold: float, k: int) -
     return out
 
 
+def run_update(masked: np.ndarray, tok: np.ndarray, conf: np.ndarray, prev_tok: np.ndarray,
+               run: np.ndarray, floor: float):
+    """Convergence runs after one step: for each masked position, the run grows by one when the
+    argmax equals the previous step's and the confidence is above ``floor``, restarts at 1 for
+    a new argmax above the floor, and is 0 at or below it (NaN included).  Positions that are not
+    masked keep their values.  Returns the new (prev_tok, run)."""
+    prev_tok = prev_tok.copy()
+    run = run.copy()
+    for i in range(masked.shape[0]):
+        if not masked[i]:
+            continue
+        above = bool(conf[i] > floor)  # False for NaN
+        if not above:
+            run[i] = 0
+        elif tok[i] == prev_tok[i]:
+            run[i] = run[i] + 1
+        else:
+            run[i] = 1
+        prev_tok[i] = tok[i]
+    return prev_tok, run
+
+
+def hard_floor(n_hard: int, spb: int, j: int) -> int:
+    """Floor of step j >= 1 of a block under first-step scheduling: the n_hard positions left
+    after the first step spread evenly over the remaining spb - 1 steps (at least 1)."""
+    return floor_count(n_hard, max(spb - 1, 1), j - 1)
+
+
 class Decoder:
     """Block-wise cached decoding of a batch of independent sequences.
 
@@ -120,6 +168,13 @@ class Decoder:
         self.j = 0
         self.pending = None
         self.forwards = {"full": 0, "cached": 0}
+        self.exit_steps = int(cfg.get("exit_steps", 0))
+        self.exit_floor = float(cfg.get("exit_floor", 0.9))
+        self.first_threshold = float(cfg.get("first_threshold", -1.0))
+        self.prev_tok = np.full((self.B, self.Bs), -1, dtype=np.int64)
+        self.run = np.zeros((self.B, self.Bs), dtype=np.int64)
+        self.n_hard = np.zeros(self.B, dtype=np.int64)
+        self.early_exits = 0
 
     # -- state ---------------------------------------------------------------------------
     def set_tokens(self, x: np.ndarray) -> None:
@@ -200,6 +255,9 @@ class Decoder:
         if not 0 <= b < self.nb:
             raise ValueError("block out of range")
         self.block, self.j = b, 0
+        self.prev_tok[:] = -1
+        self.run[:] = 0
+        self.n_hard[:] = 0
         self.pending = self._full()
 
     def step(self) -> tuple[dict, bool]:
@@ -214,14 +272,33 @@ class Decoder:
         else:
             stats = self._cached()
         s, e = self.block_range(self.block)
-        k = floor_count(self.Bs, self.spb, self.j)
+        first = self.first_threshold >= 0
+        tau = self.first_threshold if first and self.j == 0 else self.cfg["threshold"]
         committed = np.zeros((self.B, self.Bs), dtype=bool)
+        ks = np.zeros(self.B, dtype=np.int64)
+        exited = np.zeros(self.B, dtype=bool)
         for r in range(self.B):
             masked = self.x[r, s:e] == self.mask_id
-            c = commit_set(masked, stats[r]["conf"], self.cfg["threshold"], k)
-            self.x[r, s:e][c] = stats[r]["tok"][c]
+            tok, conf = stats[r]["tok"], stats[r]["conf"]
+            if first and self.j >= 1:
+                k = hard_floor(int(self.n_hard[r]), self.spb, self.j)
+            else:
+                k = floor_count(self.Bs, self.spb, self.j)
+            ks[r] = k
+            c = commit_set(masked, conf, tau, k)
+            if self.exit_steps > 0:
+                self.prev_tok[r], self.run[r] = run_update(masked, tok, conf, self.prev_tok[r],
+                                                           self.run[r], self.exit_floor)
+                rest = masked & ~c
+                if rest.any() and (self.run[r][rest] >= self.exit_steps).all():
+                    c = c | rest
+                    exited[r] = True
+                    self.early_exits += 1
+            if first and self.j == 0:
+                self.n_hard[r] = int((masked & ~c).sum())
+            self.x[r, s:e][c] = tok[c]
             committed[r] = c
-        rec = dict(block=self.block, j=self.j, k=k,
+        rec = dict(block=self.block, j=self.j, k=int(ks.max()), ks=ks, exited=exited,
                    tok=np.stack([st["tok"] for st in stats]),
                    conf=np.stack([st["conf"] for st in stats]),
                    p2=np.stack([st["p2"] for st in stats]),

@@ -28,6 +28,13 @@ use_cache
     (prefix + suffix) cache.
 weight_seed, prompt_seed, weight_std
     Generator seeds and the weight standard deviation.
+suffix_window, attention
+    Approximate suffix pruning window (< 0: whole context); "full" or "block_causal".
+exit_steps, exit_floor
+    Early exit for converged tokens: a row's block ends once every masked position kept its
+    argmax above exit_floor for exit_steps consecutive steps (0: off).
+first_threshold
+    First-step confidence scheduling: the threshold of a block's first step (< 0: off).
 """
 
 from __future__ import annotations
@@ -38,7 +45,8 @@ NO_CACHE, PREFIX_CACHE, DUAL_CACHE = 0, 1, 2
 
 _COMMON = dict(rms_eps=1e-5, rope_base=10000.0, logit_scale=20.0, steps=0, threshold=0.9,
                weight_seed=1234, prompt_seed=5678, weight_std=0.02, random_gains=False,
-               suffix_window=-1, attention="full")
+               suffix_window=-1, attention="full", exit_steps=0, exit_floor=0.9,
+               first_threshold=-1.0)
 
 CONFIGS = {
     # Tiny LLaDA-style model in fp32.

@@ -76,7 +76,8 @@ def compare_step(cfg, rec, x_before, info, logits_gpu, rep: Report, check_logits
     rep.steps += 1
     for b in range(B):
         c_ref, p2_ref = rec["conf"][b], rec["p2"][b]
-        ex_b, ex_f = exempt_masks(cfg, x_before[b], s, c_ref, p2_ref, rec["k"])
+        k = int(rec["ks"][b]) if "ks" in rec else rec["k"]
+        ex_b, ex_f = exempt_masks(cfg, x_before[b], s, c_ref, p2_ref, k)
         ex = ex_b | ex_f
         rep.exempt += int(ex_b.sum())
         rep.exempt_floor += int(ex_f.sum())
