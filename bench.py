@@ -194,6 +194,12 @@ def main():
                     help="approximate suffix pruning window (default: the workload's, -1 = off)")
     ap.add_argument("--attention", choices=["full", "block_causal"], default=None,
                     help="attention pattern (default: the workload's, full)")
+    ap.add_argument("--exit-steps", type=int, default=None,
+                    help="early exit for converged tokens: run length (default: the workload's, 0 = off)")
+    ap.add_argument("--exit-floor", type=float, default=None,
+                    help="early exit: confidence a converged token stays above")
+    ap.add_argument("--first-threshold", type=float, default=None,
+                    help="first-step confidence scheduling: first-step threshold (< 0 = off)")
     ap.add_argument("--blocks", type=int, default=0,
                     help="time prefill plus only the first N blocks (default: the whole generate)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -226,6 +232,10 @@ def main():
         cfg["suffix_window"] = args.suffix_window
     if args.attention is not None:
         cfg["attention"] = args.attention
+    for key, val in (("exit_steps", args.exit_steps), ("exit_floor", args.exit_floor),
+                     ("first_threshold", args.first_threshold)):
+        if val is not None:
+            cfg[key] = val
     nb_all = cfg["gen_length"] // cfg["block_size"]
     nblocks = args.blocks if 0 < args.blocks < nb_all else nb_all
     torch.cuda.set_device(0)
@@ -282,7 +292,8 @@ def main():
     out = {
         "metric": ("committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)"
                    if cfg["name"] == "llada8b" and cfg["suffix_window"] < 0 and nblocks == nb_all
-                   and cfg["attention"] == "full"
+                   and cfg["attention"] == "full" and cfg["exit_steps"] == 0
+                   and cfg["first_threshold"] < 0
                    else f"committed tokens/s ({cfg['name']})"),
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
@@ -293,11 +304,13 @@ def main():
                    "block_size": cfg["block_size"], "threshold": cfg["threshold"],
                    "use_cache": ["none", "prefix", "dual"][cfg["use_cache"]],
                    "suffix_window": cfg["suffix_window"], "attention": cfg["attention"],
-                   "blocks_timed": nblocks},
+                   "exit_steps": cfg["exit_steps"], "exit_floor": cfg["exit_floor"],
+                   "first_threshold": cfg["first_threshold"], "blocks_timed": nblocks},
         "roofline": roof,
         "denoise_steps_per_generate": st["steps"],
         "refreshes_per_generate": st["full_forwards"],
         "cached_steps_per_generate": st["cached_forwards"],
+        "early_exits_per_generate": st["early_exits"],
         "refresh_latency_ms": refresh_ms, "cached_step_latency_ms": step_ms,
         "phase_roofline": phase_roofline(cfg, refresh_ms, step_ms),
         "kernel_classes": {k: {"launches": v["launches"], "ms": v["ms"],

@@ -78,6 +78,9 @@ int check_cfg(const dllm_cfg *c, std::string &msg) {
   if (std::isnan(c->threshold)) return bad("threshold is NaN");
   if (c->attention < 0 || c->attention > 1) return bad("attention must be 0 (full) or 1 (block-causal)");
   if (c->use_cache < 0 || c->use_cache > 2) return bad("use_cache must be 0, 1 or 2");
+  if (c->exit_steps < 0) return bad("exit_steps must be >= 0");
+  if (std::isnan(c->exit_floor)) return bad("exit_floor is NaN");
+  if (std::isnan(c->first_threshold)) return bad("first_threshold is NaN");
   const long long L = (long long)c->prompt_len + c->gen_length;
   if (L * c->batch > (1LL << 26)) return bad("batch * (prompt_len + gen_length) too large");
   if (c->dtype == DLLM_F32 && L > 32768) return bad("f32: prompt_len + gen_length must be <= 32768");
@@ -94,7 +97,7 @@ struct Plan {
   size_t Mmax;  // rows of the largest forward (B*L)
   size_t off_x, off_k, off_v, off_cos, off_sin, off_h, off_ahi, off_alo, off_acthi, off_actlo,
       off_q, off_apart, off_gpart, off_hpart, off_tok, off_conf, off_p2, off_com,
-      off_cnt, off_wpack, off_hc, off_qc, total;
+      off_cnt, off_sched, off_wpack, off_hc, off_qc, total;
   // The scratch region [off_scratch, total): partial results that live only within one launch
   // sequence (split-K tiles, attention key-chunk partials, lm_head tile partials).  The
   // static-scratch variant takes it from the library's static device array instead.
@@ -217,8 +220,11 @@ void make_plan(const dllm_cfg *c, Plan &p) {
   p.off_conf = take((size_t)p.B * p.Bs * 4);
   p.off_p2 = take((size_t)p.B * p.Bs * 4);
   p.off_com = take((size_t)p.B * p.Bs);
-  // per batch row: committed, remaining masked and NaN-confidence counts of the last step
-  p.off_cnt = take((size_t)3 * p.B * 4);
+  // per batch row: committed, remaining masked and NaN-confidence counts of the last step, and
+  // whether it ended the row's block by the early exit
+  p.off_cnt = take((size_t)4 * p.B * 4);
+  // schedule-rule state: previous argmax and run per block position, hard positions per row
+  p.off_sched = take(((size_t)2 * p.B * p.Bs + p.B) * 4);
   // the block rows' residual stream and queries in the last layer (forward)
   p.off_hc = take((size_t)p.B * p.Bs * p.d * 4);
   p.off_qc = take((size_t)p.B * p.Bs * p.nq * 4);
@@ -253,7 +259,8 @@ struct dllm_handle {
   int *tok;
   float *conf, *p2;
   uint8_t *com;
-  int *cnt;  // [3][B]: committed, remaining masked, NaN confidences (last step)
+  int *cnt;  // [4][B]: committed, remaining masked, NaN confidences, early exit (last step)
+  int *sched;  // [B][Bs] previous argmax, [B][Bs] run, [B] hard positions (schedule rules)
   // decode state
   bool have_tokens = false;
   int block = -1, j = 0;
@@ -654,10 +661,19 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   }
   h->fresh = false;
   const int s = p.P + h->block * p.Bs;
+  CommitRules cr;
+  cr.j = h->j;
+  cr.spb = p.spb;
+  cr.exit_steps = h->cfg.exit_steps;
+  cr.exit_floor = h->cfg.exit_floor;
+  cr.first_threshold = h->cfg.first_threshold;
+  cr.prev_tok = h->sched;
+  cr.run = h->sched + (size_t)p.B * p.Bs;
+  cr.n_hard = h->sched + (size_t)2 * p.B * p.Bs;
   HIPCHK(launch_commit(h->x, p.L, p.B, s, p.Bs, h->tok, h->conf, h->cfg.threshold, floor_count(p, h->j),
-                       h->cfg.mask_id, h->com, h->cnt, h->cnt + p.B, h->cnt + 2 * p.B, h->st));
+                       h->cfg.mask_id, h->com, h->cnt, cr, h->st));
   HIPCHK(hipEventRecord(h->ev_step[1], h->st));
-  HIPCHK(hipMemcpyAsync(h->h_cnt.data(), h->cnt, (size_t)3 * p.B * 4, hipMemcpyDeviceToHost, h->st));
+  HIPCHK(hipMemcpyAsync(h->h_cnt.data(), h->cnt, (size_t)4 * p.B * 4, hipMemcpyDeviceToHost, h->st));
   HIPCHK(hipStreamSynchronize(h->st));
   if (!h->pending.empty()) {
     int prc = prof_resolve(h);
@@ -676,6 +692,7 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
     h->stats.committed += nc;
     h->stats.commits_hist[hist_bin(nc)]++;
     h->stats.nan_count += nan;
+    h->stats.early_exits += h->h_cnt[3 * p.B + b];
     if (rem) done = 0;
     if (n_committed) n_committed[b] = nc;
   }
@@ -760,7 +777,8 @@ int create_handle(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, s
   h->conf = (float *)(ws + p.off_conf); h->p2 = (float *)(ws + p.off_p2);
   h->com = (uint8_t *)(ws + p.off_com);
   h->cnt = (int *)(ws + p.off_cnt);
-  h->h_cnt.assign((size_t)3 * p.B, 0);
+  h->sched = (int *)(ws + p.off_sched);
+  h->h_cnt.assign((size_t)4 * p.B, 0);
   {
     const char *ds = getenv("DLLM_DEBUG_SYNC");
     h->debug_sync = ds && *ds && strcmp(ds, "0") != 0;

@@ -177,11 +177,24 @@ size_t attention_part_bytes(RowSet rows, int n_heads, int n_kv_heads, int head_d
 // Merge lm_head partials: tok, conf = 1/Z, p2 = exp(m2 - m1)/Z per row.
 hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int *tok, float *conf,
                              float *p2, hipStream_t st);
-// Commit for each batch row over its block [s, s+Bs); per row: positions committed, masked
-// positions left, and masked positions whose confidence is NaN.
+// Schedule rules of the commit: early exit for converged tokens (exit_steps > 0) and first-step
+// confidence scheduling (first_threshold >= 0); j is the step's index in its block, spb the
+// block's step budget.  Per-position state [B][Bs] (argmax of the previous step, run length)
+// and per-row state [B] (hard positions left after the first step) live in the workspace; the
+// first step of a block starts them afresh.
+struct CommitRules {
+  int j, spb;
+  int exit_steps;
+  float exit_floor;
+  float first_threshold;
+  int *prev_tok, *run, *n_hard;
+};
+// Commit for each batch row over its block [s, s+Bs); per row, in cnt [4][B]: positions
+// committed, masked positions left, masked positions whose confidence is NaN, 1 when the row's
+// block ended by the early exit.
 hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
-                         float threshold, int k_floor, int mask_id, uint8_t *committed,
-                         int *n_committed, int *remaining, int *n_nan, hipStream_t st);
+                         float threshold, int k_floor, int mask_id, uint8_t *committed, int *cnt,
+                         const CommitRules &cr, hipStream_t st);
 // x[b][p] = mask_id for P <= p < L (the prompt part is left as it is).
 hipError_t launch_init_tokens(int *x, int B, int P, int L, int mask_id, hipStream_t st);
 // cos/sin tables [L][hd/2] of theta = p * base^(-2i/hd), computed in fp64 on the device.

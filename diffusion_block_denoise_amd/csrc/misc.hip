@@ -206,22 +206,38 @@ hipError_t launch_head_merge(const HeadPart *part, int n_rows, int n_vtiles, int
 // ---------------------------------------------------------------------------------------------
 // Commit: one workgroup per batch row, thread i owns block position s + i.  A masked position
 // commits when conf > threshold or when fewer than k_floor masked positions rank above it
-// (confidence descending, then position ascending; NaN ranks last and is counted).
+// (confidence descending, then position ascending; NaN ranks last and is counted).  Schedule
+// rules (CommitRules): with first-step scheduling the block's first step uses first_threshold
+// and later steps' floors spread the hard positions (masked after the first step) over the
+// remaining spb - 1 steps; with early exit each masked position's run (consecutive steps with
+// the same argmax above exit_floor) is updated, and when every position still masked after the
+// commit has a run of at least exit_steps, they are all committed.
 __global__ __launch_bounds__(256) void commit_kernel(int *x, int L, int s, int Bs, const int *tok,
                                                      const float *conf, float threshold,
                                                      int k_floor, int mask_id, uint8_t *committed,
-                                                     int *n_committed, int *remaining, int *n_nan) {
+                                                     int *cnt_out, const CommitRules cr) {
   __shared__ float cs[256];
   __shared__ int ms[256];
-  __shared__ int cnt[3];
-  const int b = blockIdx.x, i = threadIdx.x;
-  if (i < 3) cnt[i] = 0;
+  __shared__ int cnt[5];  // committed, remaining, NaN, still masked, still masked and not converged
+  const int b = blockIdx.x, i = threadIdx.x, B = gridDim.x;
+  if (i < 5) cnt[i] = 0;
   __syncthreads();
-  int masked = 0;
-  float c = -INFINITY;
+  const bool first = cr.first_threshold >= 0.f;
+  const float tau = first && cr.j == 0 ? cr.first_threshold : threshold;
+  int k = k_floor;
+  if (first && cr.j >= 1) {  // the hard positions over the remaining steps
+    const int nh = cr.n_hard[b], ns = cr.spb - 1 > 1 ? cr.spb - 1 : 1;
+    const int kk = nh / ns + ((cr.j - 1) < nh % ns ? 1 : 0);
+    k = kk < 1 ? 1 : kk;
+  }
+  const size_t pi = (size_t)b * Bs + i;
+  int masked = 0, t = 0;
+  float c = -INFINITY, craw = 0.f;
   if (i < Bs) {
     masked = x[(size_t)b * L + s + i] == mask_id;
-    c = conf[(size_t)b * Bs + i];
+    t = tok[pi];
+    craw = conf[pi];
+    c = craw;
     if (c != c) {
       c = -INFINITY;
       if (masked) atomicAdd(&cnt[2], 1);
@@ -233,28 +249,47 @@ __global__ __launch_bounds__(256) void commit_kernel(int *x, int L, int s, int B
   int commit = 0;
   if (i < Bs && masked) {
     int rank = 0;
-    for (int j = 0; j < Bs; ++j)
-      rank += ms[j] && (cs[j] > c || (cs[j] == c && j < i));
-    commit = (c > threshold) || (rank < k_floor);
-    if (commit) x[(size_t)b * L + s + i] = tok[(size_t)b * Bs + i];
+    for (int q = 0; q < Bs; ++q)
+      rank += ms[q] && (cs[q] > c || (cs[q] == c && q < i));
+    commit = (c > tau) || (rank < k);
   }
-  if (i < Bs) committed[(size_t)b * Bs + i] = (uint8_t)commit;
+  if (cr.exit_steps > 0) {
+    if (i < Bs && masked) {
+      const int prev = cr.j == 0 ? -1 : cr.prev_tok[pi];
+      int r = cr.j == 0 ? 0 : cr.run[pi];
+      r = !(craw > cr.exit_floor) ? 0 : (t == prev ? r + 1 : 1);  // NaN: not above
+      cr.prev_tok[pi] = t;
+      cr.run[pi] = r;
+      if (!commit) {
+        atomicAdd(&cnt[3], 1);
+        if (r < cr.exit_steps) atomicAdd(&cnt[4], 1);
+      }
+    }
+    __syncthreads();
+    if (cnt[3] > 0 && cnt[4] == 0 && i < Bs && masked) commit = 1;  // every rest converged
+  }
+  if (commit) x[(size_t)b * L + s + i] = t;
+  if (i < Bs) committed[pi] = (uint8_t)commit;
   if (commit) atomicAdd(&cnt[0], 1);
   if (masked && !commit) atomicAdd(&cnt[1], 1);
   __syncthreads();
   if (i == 0) {
-    n_committed[b] = cnt[0];
-    remaining[b] = cnt[1];
-    n_nan[b] = cnt[2];
+    cnt_out[b] = cnt[0];
+    cnt_out[B + b] = cnt[1];
+    cnt_out[2 * B + b] = cnt[2];
+    cnt_out[3 * B + b] = cr.exit_steps > 0 && cnt[3] > 0 && cnt[4] == 0;
+    if (first && cr.j == 0) cr.n_hard[b] = cnt[1];
   }
 }
 
 hipError_t launch_commit(int *x, int L, int B, int s, int Bs, const int *tok, const float *conf,
-                         float threshold, int k_floor, int mask_id, uint8_t *committed,
-                         int *n_committed, int *remaining, int *n_nan, hipStream_t st) {
+                         float threshold, int k_floor, int mask_id, uint8_t *committed, int *cnt,
+                         const CommitRules &cr, hipStream_t st) {
   if (Bs > 256) return hipErrorInvalidValue;
+  if ((cr.exit_steps > 0 && (!cr.prev_tok || !cr.run)) || (cr.first_threshold >= 0.f && !cr.n_hard))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(256), 0, st, x, L, s, Bs, tok, conf, threshold,
-                     k_floor, mask_id, committed, n_committed, remaining, n_nan);
+                     k_floor, mask_id, committed, cnt, cr);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ class dllm_cfg(C.Structure):
                 ("block_size", C.c_int32), ("steps", C.c_int32), ("threshold", C.c_float),
                 ("use_cache", C.c_int32), ("refresh_every_step", C.c_int32),
                 ("suffix_window", C.c_int32), ("attention", C.c_int32),
+                ("exit_steps", C.c_int32), ("exit_floor", C.c_float),
+                ("first_threshold", C.c_float),
                 ("stream", C.c_void_p)]
 
 
@@ -45,7 +47,8 @@ class dllm_stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("full_forwards", C.c_int64),
                 ("cached_forwards", C.c_int64), ("committed", C.c_int64),
                 ("commits_hist", C.c_int64 * 9), ("ms_refresh", C.c_double),
-                ("ms_step", C.c_double), ("nan_count", C.c_int64)]
+                ("ms_step", C.c_double), ("nan_count", C.c_int64),
+                ("early_exits", C.c_int64)]
 
     def as_dict(self) -> dict:
         d = {k: getattr(self, k) for k, _ in self._fields_}
@@ -140,6 +143,9 @@ def make_cfg(cfg: dict, stream=None, refresh_every_step: bool = False) -> dllm_c
     c.refresh_every_step = 1 if refresh_every_step else 0
     c.suffix_window = int(cfg.get("suffix_window", -1))
     c.attention = {"full": 0, "block_causal": 1}[cfg.get("attention", "full")]
+    c.exit_steps = int(cfg.get("exit_steps", 0))
+    c.exit_floor = float(cfg.get("exit_floor", 0.9))
+    c.first_threshold = float(cfg.get("first_threshold", -1.0))
     c.stream = stream
     return c
 

@@ -94,6 +94,18 @@ extern "C" {
  *   its own block and every earlier one.  Finished blocks' K/V are final, so the
  *   refresh at block b recomputes only blocks b-1 (the prompt for b = 0) and b,
  *   and use_cache / suffix_window change nothing.
+ *   exit_steps N > 0 turns on early exit for converged tokens (ES-dLLM paper
+ *   card, Streaming-dLLM abstract: a dynamic confidence-aware strategy with an
+ *   early exit mechanism): a masked position's run counts the consecutive steps
+ *   of the block, up to this one, in which its argmax stayed the same with a
+ *   confidence strictly above exit_floor; after a step's commit, when every
+ *   position of a batch row that is still masked has a run of at least N, all
+ *   of them are committed with their argmax and the row's block ends.
+ *   first_threshold t1 >= 0 turns on first-step confidence scheduling (ES-dLLM
+ *   paper card, CAI-DLLM abstract): a block's first step commits with threshold
+ *   t1 (the easy tokens go at once); the positions still masked after it (the
+ *   hard ones) are spread over the block's remaining steps/n_blocks - 1 steps of
+ *   the budget, which sets the floor of each later step, per batch row.
  *   All batch rows share prompt_len and advance block by block together.
  */
 typedef struct dllm_cfg {
@@ -107,6 +119,9 @@ typedef struct dllm_cfg {
   int32_t refresh_every_step;
   int32_t suffix_window;
   int32_t attention; /* DLLM_ATTN_* */
+  int32_t exit_steps;    /* early exit for converged tokens (0: off)                   */
+  float exit_floor;      /* ... confidence a converged token stays above               */
+  float first_threshold; /* first-step confidence scheduling (< 0: off)                */
   void *stream;      /* hipStream_t */
 } dllm_cfg;
 
@@ -147,6 +162,8 @@ typedef struct dllm_stats {
                                cached forwards, statistics and commits       */
   int64_t nan_count;        /* masked positions whose confidence was NaN
                                (ranked last by the commit; should stay 0)    */
+  int64_t early_exits;      /* (batch row, step) pairs that ended a block by
+                               the early exit (exit_steps > 0)               */
 } dllm_stats;
 
 typedef struct dllm_handle dllm_t;

@@ -42,6 +42,8 @@ int main(void) {{
   printf("%zu %zu %zu %zu %zu\\n", offsetof(dllm_stats, commits_hist), offsetof(dllm_stats, ms_step),
          offsetof(dllm_cfg, suffix_window), offsetof(dllm_cfg, attention),
          offsetof(dllm_stats, nan_count));
+  printf("%zu %zu %zu\\n", offsetof(dllm_cfg, exit_floor), offsetof(dllm_cfg, first_threshold),
+         offsetof(dllm_stats, early_exits));
   return 0;
 }}
 """)
@@ -53,7 +55,8 @@ int main(void) {{
             C.sizeof(dllm.dllm_weights), C.sizeof(dllm.dllm_stats),
             dllm.dllm_stats.commits_hist.offset, dllm.dllm_stats.ms_step.offset,
             dllm.dllm_cfg.suffix_window.offset, dllm.dllm_cfg.attention.offset,
-            dllm.dllm_stats.nan_count.offset]
+            dllm.dllm_stats.nan_count.offset, dllm.dllm_cfg.exit_floor.offset,
+            dllm.dllm_cfg.first_threshold.offset, dllm.dllm_stats.early_exits.offset]
     assert got == want
 
 
@@ -88,6 +91,7 @@ BAD = [
     ("mask_id", -1), ("vocab", 1), ("gen_length", 60), ("block_size", 0), ("block_size", 512),
     ("steps", 6), ("steps", -4), ("use_cache", 3), ("batch", 0), ("prompt_len", -1),
     ("threshold", float("nan")), ("rms_eps", -1.0), ("rope_base", 0.0), ("attention", 2),
+    ("exit_steps", -1), ("exit_floor", float("nan")), ("first_threshold", float("nan")),
 ]
 
 
