@@ -558,21 +558,27 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Large-tile bf16 MFMA kernel for many rows (block refresh of long contexts and batches, and the
-// widest projections).  A workgroup of 8 waves (4 x 2, two per SIMD) owns a 256 x 256 tile; each
-// wave a 64 x 128 piece as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16, so a W fragment read from
-// LDS feeds 4 MFMAs (2 blocks, hi and lo) and an A fragment 4: 8 fragment reads per 16 MFMAs,
-// where 128 x 64 pieces need 10 (A comes as hi and lo planes; measured ~0.5 % faster).  K advances in stages of 32 through
-// a ring of 3 LDS slots filled straight from global memory (global_load_lds, 16 bytes per lane,
-// no register staging), 2 stages ahead; one barrier per stage; the fragment reads of the next
-// 16-wide step go out before the MFMAs of the current one.  In a slot, a [rows][32] region holds
-// row r's 16-byte chunk c at chunk position 4 r + (c ^ ((r >> 2) & 3)): 16 consecutive rows of
-// one chunk column then cover all 64 banks of the LDS (256 bytes), so the fragment reads are
-// conflict-free.  (Measured against a 4-wave version with 128 x 128 per wave: ~5 % faster, the
-// second wave per SIMD covers the barrier and fragment-read gaps.)
-static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NS = 3;
-static constexpr int BG_WGM = 4, BG_WGN = 2, BG_NT = 64 * BG_WGM * BG_WGN;  // waves, threads
-static constexpr int BG_WM = BG_BM / BG_WGM / 32, BG_WN = BG_BN / BG_WGN / 32;  // blocks per wave
+// Large-tile bf16 MFMA kernel for many rows (block refreshes, and the cached steps of large
+// batches).  A workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile; wave w owns its rows
+// 32 w .. 32 w + 31 across all 256 columns, as 1 x 8 blocks of v_mfma_f32_32x32x16_bf16
+// (accumulators: 128 registers).  K advances in stages of 32.
+//   A (hi and lo planes) goes straight from global memory into the MFMA operand registers: each
+//     lane loads its row's 8 k of a 16-k step, one stage ahead of use (a ring of 2 stages in
+//     registers).  No wave shares A rows with another, so every A element is loaded once.
+//   W is staged in LDS (a ring of 4 slots of [256 rows][32 k]), written by the waves themselves
+//     from registers (loaded a stage and a half ahead), and read as 8 fragments per 16-k step.
+// Why: with A and W both staged through LDS (by global_load_lds), the LDS took 48 KB of writes
+// and 128 KB of fragment reads per stage, and the writes of the tile loads stalled the fragment
+// reads feeding the MFMAs (measured: the same loads into registers cost ~3 %, into LDS ~19 %).
+// Now LDS carries 16 KB of W writes and 128 KB of W reads per stage, and 1.1-1.2x the MFMA rate
+// (long-context gate/up 1.29 -> 1.41 PFLOP/s executed, 768-row down 1.02 -> 1.25).  Plain
+// register loads rather than global_load_lds for W as well: with both kinds in flight the
+// compiler cannot count them in order and waits for every load at the top of each stage.
+// In a W slot, row r's 16-byte chunk c sits at chunk position 4 r + (c ^ ((r >> 2) & 3)), so the
+// fragment reads of 16 consecutive rows cover all 64 banks once (conflict-free).
+static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NSW = 4;
+static constexpr int BG_NT = 512;                 // 8 waves
+static constexpr int BG_WL = BG_BN * 4 / BG_NT;   // 16-byte W chunks per lane and stage: 2
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -582,18 +588,15 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 }
 
 __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
-  constexpr int REG = BG_BM * BG_BK * 2;     // one [256][32] bf16 region: 16 KB
-  constexpr int STAGE = 3 * REG;             // A hi, A lo, W
-  constexpr int IR = BG_BM * 4 / BG_NT;      // global_load_lds per wave and region: 2
-  constexpr int VM_STAGE = 3 * IR;           // ... and per stage
-  constexpr int LDC = 128 + 4;               // epilogue: 128 x 128 pieces of fp32
-  static_assert(2 * 128 * LDC * 4 <= BG_NS * STAGE, "two epilogue pieces must fit the ring");
-  static_assert(BG_BM == BG_BN && IR * BG_NT == BG_BM * 4, "one chunk per lane and load");
-  __shared__ __align__(1024) unsigned char smem[BG_NS * STAGE];
+  constexpr int WST = BG_BN * BG_BK * 2;   // one W slot: 16 KB
+  constexpr int LDC = 128 + 4;             // epilogue: 128 x 128 pieces of fp32
+  constexpr int EPI = 2 * 128 * LDC * 4;
+  constexpr int SMEM = BG_NSW * WST > EPI ? BG_NSW * WST : EPI;
+  constexpr int NB = BG_BN / 32;           // 32-column blocks of a wave
+  __shared__ __align__(1024) unsigned char smem[SMEM];
   float *Ct = (float *)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / BG_WGN, wn = wave % BG_WGN;
   // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
   // split covers whole columns and every row of a column is summed in the same order) and K range
   const int mt = (a.M + BG_BM - 1) / BG_BM;
@@ -610,74 +613,64 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
   int tm, tn;
   tile_coords(tile, mt, (a.N + BG_BN - 1) / BG_BN, BIG_GM, a.xcd_cols, tm, tn);
   const int m0 = tm * BG_BM, n0 = tn * BG_BN;
-  const int T = (kend - kbeg) / BG_BK;
+  const int T = (kend - kbeg) / BG_BK;  // even: K ranges are multiples of 64
 
-  // Loads: wave w's instruction j (0..IR-1) of each region fills chunk positions
-  // (IR w + j) * 64 + lane, i.e. row r = pos >> 2 and chunk c = (pos & 3) ^ ((r >> 2) & 3).  Rows
-  // past M read row M - 1 and panels past the last one read the last one (their outputs are
-  // never written).
+  // W: chunk j of this lane is chunk position (wave * BG_WL + j) * 64 + lane of a slot: row
+  // r = pos >> 2, source chunk (pos & 3) ^ ((r >> 2) & 3).  Panels past the last one read the
+  // last one (their outputs are never written).
   const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
-  size_t aoff[IR];
-  const uint16_t *wsrc[IR];
+  const uint16_t *wsrc[BG_WL];
 #pragma unroll
-  for (int j = 0; j < IR; ++j) {
-    const int pos = (wave * IR + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
-    const size_t row = a_row(a, min(m0 + r, a.M - 1));
-    aoff[j] = a.a_packed ? pa_off(row, c * 8, a.K) : row * a.lda + c * 8;
+  for (int j = 0; j < BG_WL; ++j) {
+    const int pos = (wave * BG_WL + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
     wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
   }
-  const uint16_t *ahi = (const uint16_t *)a.a_hi, *alo = (const uint16_t *)a.a_lo;
-  // stage t -> slot t % 3; past the last stage the loads re-read it (clamped, unused), so every
-  // iteration has the same number of loads in flight
-  auto issue = [&](int t) {
-    const int k0 = kbeg + min(t, T - 1) * BG_BK;
-    unsigned char *st = smem + (t % BG_NS) * STAGE + wave * (IR * 1024);
-    const size_t kw = (size_t)(k0 / PW_K) * (PW_ROWS * PW_K);
-    const size_t ka = a.a_packed ? kw : (size_t)k0;  // packed A: 32-wide blocks like W
+  s16x8 wreg[2][BG_WL];
+  auto load_w = [&](int b, int t) {  // stage t (past the last: the last again, unused)
+    const size_t kw = (size_t)((kbeg + min(t, T - 1) * BG_BK) / PW_K) * (PW_ROWS * PW_K);
 #pragma unroll
-    for (int j = 0; j < IR; ++j) {
-      __builtin_amdgcn_global_load_lds((const void *)(ahi + aoff[j] + ka), (lds_void *)(st + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(alo + aoff[j] + ka), (lds_void *)(st + REG + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(wsrc[j] + kw), (lds_void *)(st + 2 * REG + j * 1024), 16, 0, 0);
+    for (int j = 0; j < BG_WL; ++j) wreg[b][j] = *(const s16x8 *)(wsrc[j] + kw);
+  };
+  auto write_w = [&](int b, int t) {
+    unsigned char *st = smem + (t % BG_NSW) * WST + wave * (BG_WL * 1024) + lane * 16;
+#pragma unroll
+    for (int j = 0; j < BG_WL; ++j) *(s16x8 *)(st + j * 1024) = wreg[b][j];
+  };
+  // A: lane l reads row (l & 31) of the wave's 32 rows, 8 k at 8 (l >> 5) of each 16-k step.
+  // Rows past M read row M - 1 (their outputs are never written).
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const size_t row = a_row(a, min(m0 + wave * 32 + frow, a.M - 1));
+  const size_t aoff = a.a_packed ? pa_off(row, kbeg + fhalf * 8, a.K) : row * a.lda + kbeg + fhalf * 8;
+  const size_t astep = a.a_packed ? (size_t)(PW_ROWS * PW_K) : (size_t)BG_BK;  // per stage
+  const uint16_t *ahi = (const uint16_t *)a.a_hi + aoff, *alo = (const uint16_t *)a.a_lo + aoff;
+  bf16x8_t ar[2][2][2];  // [ring][plane][16-k step]
+  auto load_a = [&](int b, int t) {
+    const size_t ks = (size_t)min(t, T - 1) * astep;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      ar[b][0][kk] = *(const bf16x8_t *)(ahi + ks + kk * 16);
+      ar[b][1][kk] = *(const bf16x8_t *)(alo + ks + kk * 16);
     }
   };
-
-  f32x16 acc[BG_WM][BG_WN];
-#pragma unroll
-  for (int i = 0; i < BG_WM; ++i)
-#pragma unroll
-    for (int j = 0; j < BG_WN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // fragment rows: lane l reads row (l & 31) of each 32-row block, chunk kk * 2 + (l >> 5)
-  const int frow = lane & 31, fsw = (frow >> 2) & 3, fhalf = lane >> 5;
-  const int arow = (wm * (BG_BM / BG_WGM) + frow) * 64, wrow = (wn * (BG_BN / BG_WGN) + frow) * 64;
-  // Fragments are double-buffered per 16-wide k step: the reads of the next step go out before
-  // the MFMAs of the current one.
-  bf16x8_t fh[2][BG_WM], fl[2][BG_WM], fb[2][BG_WN];
-  auto read_frags = [&](int t, int kk, int buf) {
-    const unsigned char *st = smem + (t % BG_NS) * STAGE;
+  // W fragments: row j * 32 + (l & 31) of the slot, chunk kk * 2 + (l >> 5); double-buffered
+  const int fsw = (frow >> 2) & 3, wrow = frow * 64;
+  bf16x8_t fb[2][NB];
+  auto read_w = [&](int t, int kk, int buf) {
+    const unsigned char *st = smem + (t % BG_NSW) * WST;
     const int cb = ((kk * 2 + fhalf) ^ fsw) * 16;
 #pragma unroll
-    for (int i = 0; i < BG_WM; ++i) {
-      fh[buf][i] = *(const bf16x8_t *)(st + arow + i * 2048 + cb);
-      fl[buf][i] = *(const bf16x8_t *)(st + REG + arow + i * 2048 + cb);
-    }
-#pragma unroll
-    for (int j = 0; j < BG_WN; ++j) fb[buf][j] = *(const bf16x8_t *)(st + 2 * REG + wrow + j * 2048 + cb);
+    for (int j = 0; j < NB; ++j) fb[buf][j] = *(const bf16x8_t *)(st + wrow + j * 2048 + cb);
   };
-  auto mfmas = [&](int buf) {
+  f32x16 acc[NB];
 #pragma unroll
-    for (int i = 0; i < BG_WM; ++i)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int j = 0; j < BG_WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  auto mfmas = [&](int b, int kk, int fbuf) {
 #pragma unroll
-    for (int i = 0; i < BG_WM; ++i)
+    for (int j = 0; j < NB; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[b][0][kk], fb[fbuf][j], acc[j], 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < BG_WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NB; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[b][1][kk], fb[fbuf][j], acc[j], 0, 0, 0);
   };
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -685,53 +678,61 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // Stage t's loads are issued at stage t - 3 (the prologue issues 0..2) into slot t % 3, which
-  // every wave has finished reading at the barrier of stage t - 2's second half.  Past the last
-  // stage the loads and reads repeat clamped addresses (unused), so the wait counts are static.
-  issue(0);
-  issue(1);
-  issue(2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * VM_STAGE, 15));  // stage 0 has landed
+  // Prologue: W(0..3) into the ring, W(4) into wreg[0], A(0) into ar[0].
+  load_w(0, 0);
+  load_w(1, 1);
+  write_w(0, 0);
+  write_w(1, 1);
+  load_w(0, 2);
+  load_w(1, 3);
+  write_w(0, 2);
+  write_w(1, 3);
+  load_w(0, 4);
+  load_a(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // this wave's ring writes are done
   barrier();
-  read_frags(0, 0, 0);
-  for (int t = 0; t < T; ++t) {
-    // 2 BG_WM + BG_WN = 8 reads in flight at most (the LDS counter only counts to 15)
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // buffer 0 is in registers
-    read_frags(t, 1, 1);
+  read_w(0, 0, 0);
+  // Stage u (b = u & 1): A(u) is in ar[b] and W(u + 4) in wreg[b], both loaded in stage u - 1.
+  // The stage starts the loads of A(u + 1) and W(u + 5) (kept ahead of the MFMAs), runs the
+  // first 16-k step, waits at a barrier until every wave has read both steps of W(u), writes
+  // W(u + 4) into W(u)'s slot and runs the second step.  W(u + 1) was written three stages
+  // earlier.  Past the last stage the loads repeat it (unused), so every stage is alike.
+  auto stage = [&](int b, int u) {
+    load_a(b ^ 1, u + 1);
+    load_w(b ^ 1, u + 5);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
+    read_w(u, 1, 1);
+    mfmas(b, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // stage t + 1 has landed once only stage t + 2's loads are outstanding; all of this
-    // wave's reads of stage t are complete before the barrier
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM_STAGE, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // this wave's LDS reads and writes are done
     barrier();
-    issue(t + 3);  // into the slot of stage t
-    read_frags(min(t + 1, T - 1), 0, 0);
+    write_w(b, u + 4);
+    read_w(min(u + 1, T - 1), 0, 0);
+    mfmas(b, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int t0 = 0; t0 < T; t0 += 2) {
+    stage(0, t0);
+    stage(1, t0 + 1);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no load still writes the ring
   __syncthreads();
-  // Epilogue in 128 x 128 pieces, the two of a 128-row half at a time: the waves whose 64 x 128
-  // pieces lie in half h write them into C tiles 0 and 1 (column half q = wn), then threads
+  // Epilogue in 128 x 128 pieces, the two of a 128-row half at a time: the waves of half h write
+  // their 32 x 256 rows into C tiles 0 and 1 (columns 0..127, 128..255), then threads
   // [q NT, (q + 1) NT) run the epilogue of piece (h, q), so every thread works.
-  static_assert(BG_BN == 2 * 128 && BG_NT == 2 * NT && BG_BN / BG_WGN == 128, "two pieces per half");
-  constexpr int QR = BG_BM / BG_WGM;
+  static_assert(BG_BN == 2 * 128 && BG_NT == 2 * NT, "two pieces per half");
 #pragma unroll
   for (int h = 0; h < BG_BM / 128; ++h) {
-    const int r0 = wm * QR - h * 128;
+    const int r0 = wave * 32 - h * 128;
     if (r0 >= 0 && r0 < 128) {
-      float *Cq = Ct + wn * (128 * LDC);
 #pragma unroll
-      for (int i = 0; i < BG_WM; ++i)
+      for (int j = 0; j < NB; ++j) {
+        float *Cq = Ct + (j >> 2) * (128 * LDC);
 #pragma unroll
-        for (int j = 0; j < BG_WN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = r0 + i * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
-            Cq[row * LDC + j * 32 + frow] = acc[i][j][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + 8 * (r / 4) + 4 * fhalf + (r & 3);
+          Cq[row * LDC + (j & 3) * 32 + frow] = acc[j][r];
+        }
+      }
     }
     __syncthreads();
     const int q = tid / NT, et = tid % NT;
@@ -935,8 +936,9 @@ static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16)
 //   reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted on MI355X to the 8B-shape
 //   projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K step of 64 alone on its
 //   CU and 1.98 us when two share it (they are limited by the CU, not by latency); a 256 x 256
-//   workgroup (one per CU) 3.7 us.  The large-tile kernel serves M >= 512 when its tiles fill at
-//   least one round (at 768 rows: the gate/up projection, ~4 % faster than 128 x 128 tiles).
+//   workgroup (one per CU) 3.0 us.  The large-tile kernel serves every GEMM of 512 rows or more
+//   (faster than 128 x 128 tiles at every refresh shape measured, q/k/v at 768 rows included:
+//   164 against 197 us).
 enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3 };
 
 struct SplitPlan {
@@ -1011,7 +1013,7 @@ static double cu_makespan(long n_full, int it_full, long n_tail, int it_tail, in
 static SplitPlan tile_plan(int kind, int M, int N, int K, double *cost_out) {
   const bool big = kind == GK_BIG;
   const int bm = big ? 256 : 128, bn = big ? 256 : 128, per_cu = big ? 1 : 2;
-  const double t1 = big ? 3.7 : 1.25, t2 = 1.98;
+  const double t1 = big ? 3.0 : 1.25, t2 = 1.98;
   const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn, iters = K / 64;
   const long tiles = (long)mt * nt;
   SplitPlan best_plan{kind, 1, K, (int)tiles, N};
@@ -1066,21 +1068,14 @@ static SplitPlan tile_plan_cached(int kind, int M, int N, int K, double *cost_ou
   return pl;
 }
 
-// Kernel of a bf16 GEMM of more than 64 rows: the large-tile kernel when its 256 x 256 tiles
-// fill the CUs at least once; with fewer, the one whose split plan the CU schedule model prices
-// lower (the large-tile kernel within 2 %: at 768 rows it measured faster than the model says on
-// the output and down projections, and slower on q/k/v, as the model has it).
+// Kernel of a GEMM: fp32 SIMT for the fp32 path; the weight-streaming kernel for up to 64 rows;
+// the large-tile kernel from 512 rows; the 128 x 128 tiled kernel in between.
 static int choose_kind(int M, int N, int K, int dtype) {
+  (void)N;
   if (dtype == 0) return GK_F32;
   if (use_skinny(M, K)) return GK_SKINNY;
   if (M < 512 || K % 64) return GK_TILED;
-  const long big_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 256) return GK_BIG;
-  double c_tiled, c_big;
-  tile_plan_cached(GK_TILED, M, N, K, &c_tiled);
-  tile_plan_cached(GK_BIG, M, N, K, &c_big);
-  if (c_tiled < 0 || c_big < 0) return GK_TILED;  // many row tiles: not modelled
-  return c_big <= 1.02 * c_tiled ? GK_BIG : GK_TILED;
+  return GK_BIG;
 }
 
 static SplitPlan split_plan(int M, int N, int K, int dtype) {
