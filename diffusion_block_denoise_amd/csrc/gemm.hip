@@ -1069,12 +1069,18 @@ static SplitPlan tile_plan_cached(int kind, int M, int N, int K, double *cost_ou
 }
 
 // Kernel of a GEMM: fp32 SIMT for the fp32 path; the weight-streaming kernel for up to 64 rows;
-// the large-tile kernel from 512 rows; the 128 x 128 tiled kernel in between.
+// from 512 rows the large-tile kernel, except where its plan would split every tile K-wise while
+// the 128 x 128 plan runs most tiles whole (the q/k/v projection at 768 rows: 144 large tiles
+// split 3 ways ran 151 us plus a 27 us reduce, against 170 us for 510 whole 128 x 128 tiles and a
+// split tail); the 128 x 128 tiled kernel below 512 rows (at 256 and 384 rows the two measured
+// alike).
 static int choose_kind(int M, int N, int K, int dtype) {
-  (void)N;
   if (dtype == 0) return GK_F32;
   if (use_skinny(M, K)) return GK_SKINNY;
   if (M < 512 || K % 64) return GK_TILED;
+  const SplitPlan big = tile_plan_cached(GK_BIG, M, N, K);
+  if (big.splits > 1 && big.n_full == 0 && tile_plan_cached(GK_TILED, M, N, K).n_full > 0)
+    return GK_TILED;
   return GK_BIG;
 }
 
