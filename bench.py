@@ -65,10 +65,10 @@ def phase_latency(h, prompt, cfg, nb):
     return med(refresh), med(step)
 
 
-def counter_traffic(kernel_class):
+def counter_traffic(kernel_class, workload):
     """HBM bytes per launch of a kernel class from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when there is none or the kernel's source has changed since the
-    counters were taken (its sha256 no longer matches)."""
+    WRITE_SIZE summary of the same workload, or None when there is none or the kernel's source
+    has changed since the counters were taken (its sha256 no longer matches)."""
     import glob
     import hashlib
     import re
@@ -77,7 +77,7 @@ def counter_traffic(kernel_class):
         if not m:
             continue
         d = json.loads(m.group(1))
-        if d.get("kernel_class") != kernel_class:
+        if d.get("kernel_class") != kernel_class or d.get("workload") != workload:
             continue
         src = os.path.join(ROOT, d["source"])
         if not os.path.exists(src):
@@ -88,8 +88,9 @@ def counter_traffic(kernel_class):
     return None
 
 
-def roofline(prof, dtype):
-    """Roofline entry for the kernel class with the largest timed share."""
+def roofline(prof, dtype, workload):
+    """Roofline entry for the kernel class with the largest timed share; `workload` names the
+    run's configuration for the counter-based traffic (None: a configuration without counters)."""
     name, k = max(prof.items(), key=lambda kv: kv[1]["ms"])
     if k["launches"] == 0 or k["ms"] <= 0:
         return None, name
@@ -98,11 +99,11 @@ def roofline(prof, dtype):
         peak = BF16_PEAK_TFLOPS if dtype == "bf16" else F32_PEAK_TFLOPS
         ach = k["flops"] / t / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                "frac": ach / peak, "traffic": counter_traffic(name), "kernel": name,
+                "frac": ach / peak, "traffic": counter_traffic(name, workload), "kernel": name,
                 "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
     ach = k["bytes"] / t / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": ach / HBM_PEAK_GBS, "traffic": counter_traffic(name), "kernel": name,
+            "frac": ach / HBM_PEAK_GBS, "traffic": counter_traffic(name, workload), "kernel": name,
             "launches": k["launches"], "avg_us": k["ms"] / k["launches"] * 1e3}, name
 
 
@@ -286,14 +287,15 @@ def main():
         run()
         prof = h.get_profile()
         h.set_profiling(0)
-        roof, dom = roofline(prof, cfg["dtype"])
+    headline = (cfg["name"] == "llada8b" and cfg["suffix_window"] < 0 and nblocks == nb_all
+                and cfg["attention"] == "full" and cfg["exit_steps"] == 0
+                and cfg["first_threshold"] < 0)
+    if not args.no_profile:
+        roof, _ = roofline(prof, cfg["dtype"], "llada8b" if headline else None)
     refresh_ms, step_ms = phase_latency(h, prompt, cfg, nblocks)
     st = stats[-1]
     out = {
-        "metric": ("committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)"
-                   if cfg["name"] == "llada8b" and cfg["suffix_window"] < 0 and nblocks == nb_all
-                   and cfg["attention"] == "full" and cfg["exit_steps"] == 0
-                   and cfg["first_threshold"] < 0
+        "metric": ("committed tokens/s (LLaDA-8B shape, block 32, threshold 0.9)" if headline
                    else f"committed tokens/s ({cfg['name']})"),
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
