@@ -558,15 +558,22 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Large-tile bf16 MFMA kernel for many rows (block refreshes, and the cached steps of large
-// batches).  A workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile; wave w owns its rows
-// 32 w .. 32 w + 31 across all 256 columns, as 1 x 8 blocks of v_mfma_f32_32x32x16_bf16
-// (accumulators: 128 registers).  K advances in stages of 32.
+// Large-tile bf16 MFMA kernels for many rows (block refreshes, and the cached steps of large
+// batches).  A workgroup of NWV waves owns a (32 NWV) x BNT tile; wave w owns its rows
+// 32 w .. 32 w + 31 across all BNT columns, as 1 x (BNT / 32) blocks of
+// v_mfma_f32_32x32x16_bf16.  Two shapes: 256 x 256 (8 waves, two per SIMD, 128 accumulator
+// registers each) and 384 x 128 (12 waves, three per SIMD, 64 accumulators each), which tiles
+// a 768-row refresh projection of 12288 or 4096 columns into 192 or 64 tiles (whole rounds of the
+// XCDs' CUs with or without a K split) where 256 x 256 tiles leave a partly filled round.
+// K advances in stages of 32.
 //   A (hi and lo planes) goes straight from global memory into the MFMA operand registers: each
 //     lane loads its row's 8 k of a 16-k step, one stage ahead of use (a ring of 2 stages in
 //     registers).  No wave shares A rows with another, so every A element is loaded once.
-//   W is staged in LDS (a ring of 4 slots of [256 rows][32 k]), written by the waves themselves
-//     from registers (loaded a stage and a half ahead), and read as 8 fragments per 16-k step.
+//   W is staged in LDS (a ring of 4 slots of [BNT rows][32 k]), written by the waves themselves
+//     from registers (loaded a stage and a half ahead), and read as BNT / 32 fragments per 16-k
+//     step.  A slot is BNT / 16 loads of 1 KB (64 lanes x 16 bytes); with more waves than that
+//     the extra waves load and write a copy of another wave's part (the same bytes to the same
+//     place), so every wave runs the same unconditional code.
 // Why: with A and W both staged through LDS (by global_load_lds), the LDS took 48 KB of writes
 // and 128 KB of fragment reads per stage, and the writes of the tile loads stalled the fragment
 // reads feeding the MFMAs (measured: the same loads into registers cost ~3 %, into LDS ~19 %).
@@ -576,9 +583,7 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(const GemmArgs a) {
 // compiler cannot count them in order and waits for every load at the top of each stage.
 // In a W slot, row r's 16-byte chunk c sits at chunk position 4 r + (c ^ ((r >> 2) & 3)), so the
 // fragment reads of 16 consecutive rows cover all 64 banks once (conflict-free).
-static constexpr int BG_BM = 256, BG_BN = 256, BG_BK = 32, BG_NSW = 4;
-static constexpr int BG_NT = 512;                 // 8 waves
-static constexpr int BG_WL = BG_BN * 4 / BG_NT;   // 16-byte W chunks per lane and stage: 2
+static constexpr int BG_BK = 32, BG_NSW = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -587,19 +592,25 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
 }
 
-__global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
-  constexpr int WST = BG_BN * BG_BK * 2;   // one W slot: 16 KB
-  constexpr int LDC = 128 + 4;             // epilogue: 128 x 128 pieces of fp32
+template <int NWV, int BNT>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_big_kernel(const GemmArgs a) {
+  constexpr int BMT = 32 * NWV;            // tile rows
+  constexpr int WST = BNT * BG_BK * 2;     // one W slot
+  constexpr int WLOADS = BNT / 16;         // 1 KB loads per W slot
+  constexpr int WL = (WLOADS + NWV - 1) / NWV;  // per wave
+  constexpr int LDC = 128 + 4;             // epilogue: 128 x 128 pieces of fp32, two at a time
   constexpr int EPI = 2 * 128 * LDC * 4;
   constexpr int SMEM = BG_NSW * WST > EPI ? BG_NSW * WST : EPI;
-  constexpr int NB = BG_BN / 32;           // 32-column blocks of a wave
+  constexpr int NB = BNT / 32;             // 32-column blocks of a wave
+  constexpr int NPC = BNT / 128;           // 128-column pieces of a 128-row group
+  static_assert(BNT % 128 == 0 && BMT % 128 == 0 && 64 * NWV >= 2 * NT, "epilogue pieces");
   __shared__ __align__(1024) unsigned char smem[SMEM];
   float *Ct = (float *)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // work item -> tile (tile_coords; split tiles only occur with a single group of rows, where a
   // split covers whole columns and every row of a column is summed in the same order) and K range
-  const int mt = (a.M + BG_BM - 1) / BG_BM;
+  const int mt = (a.M + BMT - 1) / BMT;
   const int w = blockIdx.x;
   int tile = w, split = -1, kbeg = 0, kend = a.K;
   if (w >= a.n_full) {
@@ -611,30 +622,34 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
     if (a.tail_sp == 1) split = -1;
   }
   int tm, tn;
-  tile_coords(tile, mt, (a.N + BG_BN - 1) / BG_BN, BIG_GM, a.xcd_cols, tm, tn);
-  const int m0 = tm * BG_BM, n0 = tn * BG_BN;
+  tile_coords(tile, mt, (a.N + BNT - 1) / BNT, BIG_GM, a.xcd_cols, tm, tn);
+  const int m0 = tm * BMT, n0 = tn * BNT;
   const int T = (kend - kbeg) / BG_BK;  // even: K ranges are multiples of 64
 
-  // W: chunk j of this lane is chunk position (wave * BG_WL + j) * 64 + lane of a slot: row
-  // r = pos >> 2, source chunk (pos & 3) ^ ((r >> 2) & 3).  Panels past the last one read the
-  // last one (their outputs are never written).
+  // W: load j of this wave fills 1 KB block (wave * WL + j) % WLOADS of a slot; its lane's chunk
+  // position there is pos = block * 64 + lane: row r = pos >> 2, source chunk (pos & 3) ^
+  // ((r >> 2) & 3).  Panels past the last one read the last one (their outputs are never
+  // written).
   const int last_panel = (a.N + PW_ROWS - 1) / PW_ROWS - 1;
-  const uint16_t *wsrc[BG_WL];
+  const uint16_t *wsrc[WL];
+  int wdst[WL];
 #pragma unroll
-  for (int j = 0; j < BG_WL; ++j) {
-    const int pos = (wave * BG_WL + j) * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
+  for (int j = 0; j < WL; ++j) {
+    const int blk = (wave * WL + j) % WLOADS;
+    const int pos = blk * 64 + lane, r = pos >> 2, c = (pos & 3) ^ ((r >> 2) & 3);
     wsrc[j] = wp_block(a, min(n0 / PW_ROWS + (r >> 7), last_panel), 0) + (r & 127) * PW_K + c * 8;
+    wdst[j] = blk * 1024 + lane * 16;
   }
-  s16x8 wreg[2][BG_WL];
+  s16x8 wreg[2][WL];
   auto load_w = [&](int b, int t) {  // stage t (past the last: the last again, unused)
     const size_t kw = (size_t)((kbeg + min(t, T - 1) * BG_BK) / PW_K) * (PW_ROWS * PW_K);
 #pragma unroll
-    for (int j = 0; j < BG_WL; ++j) wreg[b][j] = *(const s16x8 *)(wsrc[j] + kw);
+    for (int j = 0; j < WL; ++j) wreg[b][j] = *(const s16x8 *)(wsrc[j] + kw);
   };
   auto write_w = [&](int b, int t) {
-    unsigned char *st = smem + (t % BG_NSW) * WST + wave * (BG_WL * 1024) + lane * 16;
+    unsigned char *st = smem + (t % BG_NSW) * WST;
 #pragma unroll
-    for (int j = 0; j < BG_WL; ++j) *(s16x8 *)(st + j * 1024) = wreg[b][j];
+    for (int j = 0; j < WL; ++j) *(s16x8 *)(st + wdst[j]) = wreg[b][j];
   };
   // A: lane l reads row (l & 31) of the wave's 32 rows, 8 k at 8 (l >> 5) of each 16-k step.
   // Rows past M read row M - 1 (their outputs are never written).
@@ -716,31 +731,36 @@ __global__ __launch_bounds__(BG_NT, 1) void gemm_big_kernel(const GemmArgs a) {
     stage(1, t0 + 1);
   }
   __syncthreads();
-  // Epilogue in 128 x 128 pieces, the two of a 128-row half at a time: the waves of half h write
-  // their 32 x 256 rows into C tiles 0 and 1 (columns 0..127, 128..255), then threads
-  // [q NT, (q + 1) NT) run the epilogue of piece (h, q), so every thread works.
-  static_assert(BG_BN == 2 * 128 && BG_NT == 2 * NT, "two pieces per half");
+  // Epilogue in 128 x 128 pieces, two at a time: piece (g, c) is rows 128 g.., columns 128 c..
+  // of the tile, numbered g * NPC + c.  In pass p the waves holding rows of pieces 2p and 2p + 1
+  // write them into C tiles 0 and 1, then threads [q NT, (q + 1) NT) run the epilogue of piece
+  // 2p + q (with 256 x 256 tiles: both pieces of a 128-row half, every thread working).
+  constexpr int NPIECE = BMT / 128 * NPC;
 #pragma unroll
-  for (int h = 0; h < BG_BM / 128; ++h) {
-    const int r0 = wave * 32 - h * 128;
-    if (r0 >= 0 && r0 < 128) {
+  for (int pass = 0; pass < (NPIECE + 1) / 2; ++pass) {
+    const int g = wave / 4;  // this wave's 128-row group
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        float *Cq = Ct + (j >> 2) * (128 * LDC);
+    for (int j = 0; j < NB; ++j) {
+      const int slot = g * NPC + (j >> 2) - 2 * pass;
+      if (slot == 0 || slot == 1) {
+        float *Cq = Ct + slot * (128 * LDC);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = r0 + 8 * (r / 4) + 4 * fhalf + (r & 3);
+          const int row = (wave & 3) * 32 + 8 * (r / 4) + 4 * fhalf + (r & 3);
           Cq[row * LDC + (j & 3) * 32 + frow] = acc[j][r];
         }
       }
     }
     __syncthreads();
-    const int q = tid / NT, et = tid % NT;
-    const float *Cq = Ct + q * (128 * LDC);
-    if (split >= 0)
-      write_partial<128, 128>(a, split, Cq, LDC, m0 + h * 128, n0 + q * 128, et);
-    else
-      run_epilogue<bf16, 128, 128>(a, Cq, LDC, m0 + h * 128, n0 + q * 128, et);
+    const int q = tid / NT, et = tid % NT, pc = 2 * pass + q;
+    if (q < 2 && pc < NPIECE) {
+      const float *Cq = Ct + q * (128 * LDC);
+      const int pm = m0 + (pc / NPC) * 128, pn = n0 + (pc % NPC) * 128;
+      if (split >= 0)
+        write_partial<128, 128>(a, split, Cq, LDC, pm, pn, et);
+      else
+        run_epilogue<bf16, 128, 128>(a, Cq, LDC, pm, pn, et);
+    }
     __syncthreads();
   }
 }
@@ -931,15 +951,15 @@ static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16)
 //   Tiled (128 x 128) and large-tile (256 x 256) kernels: the first n_full work items are whole
 //   tiles (whole columns of M tiles) and the remaining columns are split tail_sp ways, so that
 //   the last, partly filled round of resident workgroups is spread over the whole GPU.  The plan
-//   minimises an estimate of the time: the work items, in launch order, placed on the 256 CUs
-//   (cu_makespan), plus the round trip of the fp32 partial tiles (written here, read by the
+//   minimises an estimate of the time: the work items, in launch order, placed on the 32 CUs of
+//   the XCD each one runs on (gpu_makespan), plus the round trip of the fp32 partial tiles (written here, read by the
 //   reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted on MI355X to the 8B-shape
 //   projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K step of 64 alone on its
 //   CU and 1.98 us when two share it (they are limited by the CU, not by latency); a 256 x 256
 //   workgroup (one per CU) 3.0 us.  The large-tile kernel serves every GEMM of 512 rows or more
 //   (faster than 128 x 128 tiles at every refresh shape measured, q/k/v at 768 rows included:
 //   164 against 197 us).
-enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3 };
+enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3, GK_BIG384 = 4 };
 
 struct SplitPlan {
   int kind;     // GemmKind
@@ -1010,10 +1030,30 @@ static double cu_makespan(long n_full, int it_full, long n_tail, int it_tail, in
   return end;
 }
 
+// The same over the whole GPU: workgroup i of a launch runs on XCD i % 8, and each XCD hands its
+// own workgroups, in launch order, to its 32 CUs, so the XCDs are scheduled independently and the
+// launch ends with the slowest.  (A single queue over 256 CUs would let an XCD with idle CUs take
+// another XCD's items: the 768-row gate/up plan then looked balanced, while the XCDs holding a
+// 33rd tail item each ran a third round of them: 284 us in place of ~256, measured per workgroup.)
+static double gpu_makespan(long n_full, int it_full, long n_tail, int it_tail, int per_cu,
+                           double t1, double t2) {
+  auto count = [](long n, int x) { return n > x ? (n - x + 7) / 8 : 0L; };  // i < n, i % 8 == x
+  double end = 0.0;
+  for (int x = 0; x < 8; ++x) {
+    const long nf = count(n_full, x), nt = count(n_full + n_tail, x) - nf;
+    end = std::max(end, cu_makespan(nf, it_full, nt, it_tail, 32, per_cu, t1, t2));
+  }
+  return end;
+}
+
+// Tile rows and columns of the tiled and large-tile kernels.
+static int tile_bm(int kind) { return kind == GK_BIG ? 256 : kind == GK_BIG384 ? 384 : 128; }
+static int tile_bn(int kind) { return kind == GK_BIG ? 256 : 128; }
+
 static SplitPlan tile_plan(int kind, int M, int N, int K, double *cost_out) {
-  const bool big = kind == GK_BIG;
-  const int bm = big ? 256 : 128, bn = big ? 256 : 128, per_cu = big ? 1 : 2;
-  const double t1 = big ? 3.0 : 1.25, t2 = 1.98;
+  const bool big = kind == GK_BIG || kind == GK_BIG384;
+  const int bm = tile_bm(kind), bn = tile_bn(kind), per_cu = big ? 1 : 2;
+  const double t1 = kind == GK_BIG ? 3.0 : kind == GK_BIG384 ? 2.4 : 1.25, t2 = 1.98;
   const int mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn, iters = K / 64;
   const long tiles = (long)mt * nt;
   SplitPlan best_plan{kind, 1, K, (int)tiles, N};
@@ -1032,7 +1072,7 @@ static SplitPlan tile_plan(int kind, int M, int N, int K, double *cost_out) {
     for (int sp = 1; sp <= max_sp; ++sp) {
       const int kc = ((K + sp - 1) / sp + 63) / 64 * 64, splits = (K + kc - 1) / kc;
       if (splits != sp) continue;
-      const double span = cu_makespan(n_full, iters, n_tail_tiles * splits, kc / 64, 256, per_cu, t1, t2);
+      const double span = gpu_makespan(n_full, iters, n_tail_tiles * splits, kc / 64, per_cu, t1, t2);
       const int tail_cols = N - c * bn;
       const double partial_us = splits > 1 ? splits * (double)M * tail_cols * 8.0 / 6.0e6 + 4.0 : 0.0;
       const double cost = span + partial_us;
@@ -1069,19 +1109,27 @@ static SplitPlan tile_plan_cached(int kind, int M, int N, int K, double *cost_ou
 }
 
 // Kernel of a GEMM: fp32 SIMT for the fp32 path; the weight-streaming kernel for up to 64 rows;
-// from 512 rows the large-tile kernel, except where its plan would split every tile K-wise while
-// the 128 x 128 plan runs most tiles whole (the q/k/v projection at 768 rows: 144 large tiles
-// split 3 ways ran 151 us plus a 27 us reduce, against 170 us for 510 whole 128 x 128 tiles and a
-// split tail); the 128 x 128 tiled kernel below 512 rows (at 256 and 384 rows the two measured
-// alike).
+// from 512 rows a large-tile kernel: 256 x 256 tiles where there are many rounds of them, else
+// whichever of the 256 x 256 and 384 x 128 tiles the plan model prices lower (at 768 rows the
+// 384 x 128 tiles take q/k/v as 192 whole tiles, 161 against 167 us for 144 large tiles split 3
+// ways with their reduce and 205 us for 128 x 128 tiles, and o and down split 4 ways: 49 and
+// 126 us against 52 and 131 us; gate/up stays on 256 x 256 tiles, 293 against 300 us; measured
+// in isolation with random data), and the 128 x 128 kernel where that plan would split every
+// tile K-wise while the 128 x 128 plan runs most tiles whole; the 128 x 128 tiled kernel below
+// 512 rows (at 256 and 384 rows it and the 256 x 256 kernel measured alike).
 static int choose_kind(int M, int N, int K, int dtype) {
   if (dtype == 0) return GK_F32;
   if (use_skinny(M, K)) return GK_SKINNY;
   if (M < 512 || K % 64) return GK_TILED;
-  const SplitPlan big = tile_plan_cached(GK_BIG, M, N, K);
+  double c256, c384;
+  const SplitPlan p256 = tile_plan_cached(GK_BIG, M, N, K, &c256);
+  if (c256 < 0) return GK_BIG;  // many rounds of tiles (not modelled): the faster tile
+  const SplitPlan p384 = tile_plan_cached(GK_BIG384, M, N, K, &c384);
+  const bool t384 = c384 >= 0 && c384 < c256;
+  const SplitPlan &big = t384 ? p384 : p256;
   if (big.splits > 1 && big.n_full == 0 && tile_plan_cached(GK_TILED, M, N, K).n_full > 0)
     return GK_TILED;
-  return GK_BIG;
+  return t384 ? GK_BIG384 : GK_BIG;
 }
 
 static SplitPlan split_plan(int M, int N, int K, int dtype) {
@@ -1114,7 +1162,10 @@ size_t gemm_partial_bytes(int M, int N, int K, int dtype) {
   return (size_t)pl.splits * M * (N - pl.n_tail0) * sizeof(float);
 }
 
-bool gemm_a_packed(int M, int N, int K, int dtype) { return choose_kind(M, N, K, dtype) == GK_BIG; }
+bool gemm_a_packed(int M, int N, int K, int dtype) {
+  const int kind = choose_kind(M, N, K, dtype);
+  return kind == GK_BIG || kind == GK_BIG384;
+}
 
 int gemm_kind(int M, int K, int dtype) {
   if (dtype == 0) return 0;
@@ -1176,16 +1227,18 @@ hipError_t launch_gemm(const GemmArgs &a0, int dtype, hipStream_t st, int *split
     }
     return hipGetLastError();
   }
-  const int bt = pl.kind == GK_BIG ? 256 : 128;
-  const int mt = (a.M + bt - 1) / bt, nt = (a.N + bt - 1) / bt;
+  const int bmt = tile_bm(pl.kind), bnt = tile_bn(pl.kind);
+  const int mt = (a.M + bmt - 1) / bmt, nt = (a.N + bnt - 1) / bnt;
   a.n_full = pl.n_full;
   a.tail_sp = pl.splits;
   a.n_tail0 = pl.n_tail0;
   // columns placed XCD by XCD: the whole-tile columns (all of them without splits)
-  a.xcd_cols = (mt <= (pl.kind == GK_BIG ? BIG_GM : TILED_GM) ? pl.n_full / mt : nt) / 8 * 8;
+  a.xcd_cols = (mt <= (pl.kind == GK_TILED ? TILED_GM : BIG_GM) ? pl.n_full / mt : nt) / 8 * 8;
   const long items = (long)pl.n_full + ((long)mt * nt - pl.n_full) * pl.splits;
   if (pl.kind == GK_BIG)
-    hipLaunchKernelGGL(gemm_big_kernel, dim3((unsigned)items), dim3(BG_NT), 0, st, a);
+    hipLaunchKernelGGL((gemm_big_kernel<8, 256>), dim3((unsigned)items), dim3(512), 0, st, a);
+  else if (pl.kind == GK_BIG384)
+    hipLaunchKernelGGL((gemm_big_kernel<12, 128>), dim3((unsigned)items), dim3(768), 0, st, a);
   else
     hipLaunchKernelGGL((gemm_mfma_kernel<128, 128, 2, 2>), dim3((unsigned)items), dim3(NT), 0, st, a);
   if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
