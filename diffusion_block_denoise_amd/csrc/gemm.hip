@@ -948,17 +948,15 @@ static int bm_for(int M, int K) { return use_skinny(M, K) ? 16 * ((M + 15) / 16)
 //   Skinny kernel (M <= 64): the fewest power-of-two splits (every tile split alike) that give
 //   at least 192 workgroups, with whole stages per split; if K has too few factors of two, as
 //   many stage-aligned splits as reach 192 workgroups (or one stage each).
-//   Tiled (128 x 128) and large-tile (256 x 256) kernels: the first n_full work items are whole
-//   tiles (whole columns of M tiles) and the remaining columns are split tail_sp ways, so that
-//   the last, partly filled round of resident workgroups is spread over the whole GPU.  The plan
-//   minimises an estimate of the time: the work items, in launch order, placed on the 32 CUs of
-//   the XCD each one runs on (gpu_makespan), plus the round trip of the fp32 partial tiles (written here, read by the
-//   reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted on MI355X to the 8B-shape
-//   projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K step of 64 alone on its
-//   CU and 1.98 us when two share it (they are limited by the CU, not by latency); a 256 x 256
-//   workgroup (one per CU) 3.0 us.  The large-tile kernel serves every GEMM of 512 rows or more
-//   (faster than 128 x 128 tiles at every refresh shape measured, q/k/v at 768 rows included:
-//   164 against 197 us).
+//   Tiled (128 x 128) and large-tile (256 x 256, 384 x 128) kernels: the first n_full work items
+//   are whole tiles (whole columns of M tiles) and the remaining columns are split tail_sp ways,
+//   so that the last, partly filled round of resident workgroups is spread over the whole GPU.
+//   The plan minimises an estimate of the time: the work items, in launch order, placed on the
+//   32 CUs of the XCD each one runs on (gpu_makespan), plus the round trip of the fp32 partial
+//   tiles (written here, read by the reduce) at ~6 TB/s and ~4 us for the reduce launch.  Fitted
+//   on MI355X to the 8B-shape projections at 768 rows: a 128 x 128 workgroup takes 1.25 us per K
+//   step of 64 alone on its CU and 1.98 us when two share it (they are limited by the CU, not by
+//   latency); a 256 x 256 workgroup (one per CU) 3.0 us, a 384 x 128 one 2.4 us.
 enum GemmKind { GK_F32 = 0, GK_SKINNY = 1, GK_TILED = 2, GK_BIG = 3, GK_BIG384 = 4 };
 
 struct SplitPlan {
