@@ -3,7 +3,8 @@ benchmark uses, teacher-forced against the oracle.
 
 * LLaDA-8B shape (batch 1, 768 positions, dual cache): blocks 0, 4 and 7 (the first, a middle
   and the last block: the longest suffix and the longest prefix), the refresh and every cached
-  step until the block is committed.
+  step until the block is committed; block 4 again with early exit for converged tokens and
+  first-step confidence scheduling on.
 * Dream-7B shape (28/4 grouped heads, batch 8, 1536 positions): the GPU runs all 8 rows; the
   oracle follows batch rows 0 and 7 (rows are independent) at blocks 0, 8 and 15, for the
   refresh and one cached step.
@@ -104,10 +105,12 @@ def _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep):
         j += 1
         if done or (n_steps is not None and j >= n_steps):
             break
+    return dec
 
 
-def _run(cfg, cases):
-    """cases: (rows, block, n_steps) each; one handle, one report."""
+def _run(cfg, cases, decoders=None):
+    """cases: (rows, block, n_steps) each; one handle, one report.  `decoders` (a list) receives
+    each case's oracle decoder."""
     from diffusion_block_denoise_amd import dllm
     _log(f"case {cfg['name']} ({cfg['n_layers']} layers): weights")
     W = _weights(cfg)
@@ -115,7 +118,9 @@ def _run(cfg, cases):
     Wh = _host_weights_checked(cfg, W)
     rep = Report()
     for rows, block, n_steps in cases:
-        _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep)
+        dec = _teacher_forced(cfg, h, Wh, rows, block, n_steps, rep)
+        if decoders is not None:
+            decoders.append(dec)
     h.destroy()
     return rep
 
@@ -123,6 +128,16 @@ def _run(cfg, cases):
 def test_llada8b_first_middle_last_blocks():
     cfg = synth.configs.get("llada8b")
     rep = _run(cfg, [((0,), 0, None), ((0,), 4, None), ((0,), 7, None)])
+    assert_report(cfg, rep)
+
+
+def test_llada8b_schedule_rules_middle_block():
+    """Early exit for converged tokens and first-step confidence scheduling at the full LLaDA-8B
+    shape: block 4 until it is committed."""
+    cfg = synth.configs.get("llada8b", exit_steps=2, exit_floor=0.5, first_threshold=0.7)
+    decs = []
+    rep = _run(cfg, [((0,), 4, None)], decs)
+    _log(f"oracle early exits: {decs[0].early_exits}")
     assert_report(cfg, rep)
 
 
