@@ -131,14 +131,19 @@ def test_llada8b_first_middle_last_blocks():
     assert_report(cfg, rep)
 
 
-def test_llada8b_schedule_rules_middle_block():
+@pytest.mark.parametrize("kw,exits", [(dict(exit_steps=2, exit_floor=0.5, first_threshold=0.7), 0),
+                                      (dict(threshold=0.999, exit_steps=2, exit_floor=0.0), 1)])
+def test_llada8b_schedule_rules_middle_block(kw, exits):
     """Early exit for converged tokens and first-step confidence scheduling at the full LLaDA-8B
-    shape: block 4 until it is committed."""
-    cfg = synth.configs.get("llada8b", exit_steps=2, exit_floor=0.5, first_threshold=0.7)
+    shape: block 4 until it is committed.  With first-step scheduling the block ends in three
+    steps, before any run of unchanged argmaxes completes; with threshold 0.999 (one or two
+    commits a step) the early exit ends it (`exits`: the oracle's count in this seeded case)."""
+    cfg = synth.configs.get("llada8b", **kw)
     decs = []
     rep = _run(cfg, [((0,), 4, None)], decs)
     _log(f"oracle early exits: {decs[0].early_exits}")
     assert_report(cfg, rep)
+    assert decs[0].early_exits == exits
 
 
 def test_dream7b_rows_0_and_7():
