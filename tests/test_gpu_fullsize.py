@@ -136,7 +136,7 @@ def test_llada8b_first_middle_last_blocks():
 def test_llada8b_schedule_rules_middle_block(kw, exits):
     """Early exit for converged tokens and first-step confidence scheduling at the full LLaDA-8B
     shape: block 4 until it is committed.  With first-step scheduling the block ends in three
-    steps, before any run of unchanged argmaxes completes; with threshold 0.999 (one or two
+    steps, before any run of unchanged argmaxes completes; with threshold 0.999 (two or three
     commits a step) the early exit ends it (`exits`: the oracle's count in this seeded case)."""
     cfg = synth.configs.get("llada8b", **kw)
     decs = []
