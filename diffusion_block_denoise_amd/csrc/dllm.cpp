@@ -269,6 +269,9 @@ struct dllm_handle {
   RowSet last_rows{};
   dllm_stats stats{};
   std::vector<int> h_cnt;
+  // [4][B] counts in pinned host memory, written by the commit kernel itself (handles made by
+  // dllm_create; a static-scratch handle allocates nothing and copies cnt into h_cnt instead)
+  int *h_cnt_pin = nullptr, *d_cnt_pin = nullptr;
   std::string err;
   // GPU time of the refreshes and steps: event pairs on the stream, read at the next
   // synchronisation (dllm_block_begin is asynchronous)
@@ -287,6 +290,7 @@ struct dllm_handle {
   std::vector<Pending> pending;
   dllm_kernel_prof prof[DLLM_KC_COUNT] = {};
   ~dllm_handle() {
+    if (h_cnt_pin) (void)hipHostFree(h_cnt_pin);
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
     for (hipEvent_t e : {ev_ref[0], ev_ref[1], ev_step[0], ev_step[1]})
       if (e) (void)hipEventDestroy(e);
@@ -671,10 +675,12 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   cr.run = h->sched + (size_t)p.B * p.Bs;
   cr.n_hard = h->sched + (size_t)2 * p.B * p.Bs;
   HIPCHK(launch_commit(h->x, p.L, p.B, s, p.Bs, h->tok, h->conf, h->cfg.threshold, floor_count(p, h->j),
-                       h->cfg.mask_id, h->com, h->cnt, cr, h->st));
+                       h->cfg.mask_id, h->com, h->d_cnt_pin ? h->d_cnt_pin : h->cnt, cr, h->st));
   HIPCHK(hipEventRecord(h->ev_step[1], h->st));
-  HIPCHK(hipMemcpyAsync(h->h_cnt.data(), h->cnt, (size_t)4 * p.B * 4, hipMemcpyDeviceToHost, h->st));
+  if (!h->d_cnt_pin)
+    HIPCHK(hipMemcpyAsync(h->h_cnt.data(), h->cnt, (size_t)4 * p.B * 4, hipMemcpyDeviceToHost, h->st));
   HIPCHK(hipStreamSynchronize(h->st));
+  const int *cnt = h->h_cnt_pin ? h->h_cnt_pin : h->h_cnt.data();
   if (!h->pending.empty()) {
     int prc = prof_resolve(h);
     if (prc) return prc;
@@ -688,11 +694,11 @@ int do_step(dllm_t *h, int32_t *n_committed, int32_t *block_done) {
   h->stats.steps++;
   int done = 1;
   for (int b = 0; b < p.B; ++b) {
-    const int nc = h->h_cnt[b], rem = h->h_cnt[p.B + b], nan = h->h_cnt[2 * p.B + b];
+    const int nc = cnt[b], rem = cnt[p.B + b], nan = cnt[2 * p.B + b];
     h->stats.committed += nc;
     h->stats.commits_hist[hist_bin(nc)]++;
     h->stats.nan_count += nan;
-    h->stats.early_exits += h->h_cnt[3 * p.B + b];
+    h->stats.early_exits += cnt[3 * p.B + b];
     if (rem) done = 0;
     if (n_committed) n_committed[b] = nc;
   }
@@ -792,6 +798,14 @@ int create_handle(const dllm_weights *w, const dllm_cfg *cfg, void *workspace, s
   hipError_t e;
   for (hipEvent_t *ev : {&h->ev_ref[0], &h->ev_ref[1], &h->ev_step[0], &h->ev_step[1]})
     if ((e = hipEventCreate(ev)) != hipSuccess) return fail(e, "event");
+  if (!scratch) {
+    // the step's counts go straight to pinned host memory (no copy command before the host
+    // reads them); the static-scratch variant allocates nothing and keeps the copy
+    if ((e = hipHostMalloc((void **)&h->h_cnt_pin, (size_t)4 * p.B * sizeof(int), hipHostMallocDefault)) != hipSuccess)
+      return fail(e, "pinned counts");
+    if ((e = hipHostGetDevicePointer((void **)&h->d_cnt_pin, h->h_cnt_pin, 0)) != hipSuccess)
+      return fail(e, "pinned counts");
+  }
   if ((e = launch_fill_u32((uint32_t *)h->kc, 0, (p.off_cos - p.off_k) / 4, h->st)) != hipSuccess)
     return fail(e, "zero cache");
   if ((e = launch_rope_table(h->cos_t, h->sin_t, p.L, p.hd, cfg->rope_base, h->st)) != hipSuccess)
