@@ -55,6 +55,28 @@ def test_tiny_f32_teacher_forced_all_blocks():
     assert_report(cfg, rep)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(prompt_len=0),                                   # no prompt: the first block starts at 0
+    dict(prompt_len=0, use_cache=1),
+    dict(prompt_len=0, use_cache=0),
+    dict(block_size=1, gen_length=8),                     # one position per block
+    dict(gen_length=16, block_size=16),                   # a single block
+    dict(block_size=64, gen_length=64, use_cache=1),      # the whole generation in one block
+    dict(steps=16),                                       # 4 steps per 16-wide block: floor 4
+])
+def test_tiny_f32_edge_configs_exact(kw):
+    """Degenerate shapes of the decode: the GPU's token sequence and step count equal the
+    oracle's exactly."""
+    cfg = synth.configs.get("tiny_f32", **kw)
+    _log("case tiny_f32 edge", kw)
+    x_gpu, st = _handle(cfg).generate(synth.prompt_np(cfg))
+    dec = oracle_decoder(cfg, keep_logits=False)
+    x_ref, recs = dec.generate(synth.prompt_np(cfg))
+    assert np.array_equal(x_gpu, x_ref)
+    assert st["steps"] == len(recs)
+    assert (x_gpu[:, cfg["prompt_len"]:] != cfg["mask_id"]).all()
+
+
 # ------------------------------------------------------------------------------ bf16
 @pytest.mark.parametrize("variant", [
     dict(),                                                  # GQA 8/2, hd 32, dual, batch 2
@@ -63,6 +85,8 @@ def test_tiny_f32_teacher_forced_all_blocks():
     dict(batch=5, block_size=32, gen_length=64, prompt_len=17),  # M = 160 rows, ragged L
     dict(block_size=64, gen_length=64, batch=1, threshold=0.5),  # 64-wide block
     dict(vocab=1001, mask_id=1000),  # vocabulary not a multiple of 4: ragged split-K partials
+    dict(prompt_len=0, batch=3),  # no prompt
+    dict(block_size=256, gen_length=256, prompt_len=8, batch=1),  # the widest block, one block
 ])
 def test_bf16_teacher_forced(variant):
     cfg = small_bf16(**variant)
