@@ -87,6 +87,8 @@ def test_tiny_f32_edge_configs_exact(kw):
     dict(vocab=1001, mask_id=1000),  # vocabulary not a multiple of 4: ragged split-K partials
     dict(prompt_len=0, batch=3),  # no prompt
     dict(block_size=256, gen_length=256, prompt_len=8, batch=1),  # the widest block, one block
+    dict(n_heads=16, n_kv_heads=2),  # GQA ratio 8 (q width 512 over d_model 256)
+    dict(block_size=1, gen_length=8, batch=1),  # one row in the cached step's GEMMs
 ])
 def test_bf16_teacher_forced(variant):
     cfg = small_bf16(**variant)
