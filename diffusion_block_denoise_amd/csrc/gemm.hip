@@ -641,16 +641,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_big_kernel(const GemmArgs a)
     wdst[j] = blk * 1024 + lane * 16;
   }
   s16x8 wreg[2][WL];
-  auto load_w = [&](int b, int t) {  // stage t (past the last: the last again, unused)
+  auto load_w_to = [&](s16x8 *dst, int t) {  // stage t (past the last: the last again, unused)
     const size_t kw = (size_t)((kbeg + min(t, T - 1) * BG_BK) / PW_K) * (PW_ROWS * PW_K);
 #pragma unroll
-    for (int j = 0; j < WL; ++j) wreg[b][j] = *(const s16x8 *)(wsrc[j] + kw);
+    for (int j = 0; j < WL; ++j) dst[j] = *(const s16x8 *)(wsrc[j] + kw);
   };
-  auto write_w = [&](int b, int t) {
+  auto write_w_from = [&](const s16x8 *src, int t) {
     unsigned char *st = smem + (t % BG_NSW) * WST;
 #pragma unroll
-    for (int j = 0; j < WL; ++j) *(s16x8 *)(st + wdst[j]) = wreg[b][j];
+    for (int j = 0; j < WL; ++j) *(s16x8 *)(st + wdst[j]) = src[j];
   };
+  auto load_w = [&](int b, int t) { load_w_to(wreg[b], t); };
+  auto write_w = [&](int b, int t) { write_w_from(wreg[b], t); };
   // A: lane l reads row (l & 31) of the wave's 32 rows, 8 k at 8 (l >> 5) of each 16-k step.
   // Rows past M read row M - 1 (their outputs are never written).
   const int frow = lane & 31, fhalf = lane >> 5;
@@ -693,17 +695,21 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_big_kernel(const GemmArgs a)
     asm volatile("" ::: "memory");
   };
 
-  // Prologue: W(0..3) into the ring, W(4) into wreg[0], A(0) into ar[0].
-  load_w(0, 0);
-  load_w(1, 1);
-  write_w(0, 0);
-  write_w(1, 1);
-  load_w(0, 2);
-  load_w(1, 3);
-  write_w(0, 2);
-  write_w(1, 3);
-  load_w(0, 4);
+  // Prologue: A(0) into ar[0], W(0..3) into the ring (all of them loaded before the first is
+  // written: one memory round trip), W(4) into wreg[0].
   load_a(0, 0);
+  {
+    s16x8 wpre[2][WL];
+    load_w(0, 0);
+    load_w(1, 1);
+    load_w_to(wpre[0], 2);
+    load_w_to(wpre[1], 3);
+    write_w(0, 0);
+    write_w(1, 1);
+    write_w_from(wpre[0], 2);
+    write_w_from(wpre[1], 3);
+  }
+  load_w(0, 4);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // this wave's ring writes are done
   barrier();
   read_w(0, 0, 0);
