@@ -53,10 +53,11 @@ static inline void attn_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk)
 // them); 0: the few-query kernel.
 static inline int aw_group(int nqt) { return nqt >= 4 ? 4 : nqt >= 2 ? 2 : 0; }
 
-// Many-query kernel (one workgroup per CU): split the keys only when the workgroups fill less
-// than half of the 256 CUs.  A workgroup's time per key tile hardly changes with the number of
-// workgroups (measured: 768 queries x 32 heads, 192 workgroups, 79 us whole; 4 chunks 70 us
-// plus 21 us to merge), so splitting pays only when most CUs would idle.
+// Many-query kernel (one workgroup per CU with four query tiles, two with two): split the keys
+// only when the workgroups fill less than half of the 256 CUs.  A workgroup's time per key tile
+// hardly changes with the number of workgroups (measured: 768 queries x 32 heads, 192
+// workgroups, 79 us whole; 4 chunks 70 us plus 21 us to merge), so splitting pays only when
+// most CUs would idle.
 static inline void attn_wide_plan(RowSet rs, int H, int Hkv, int &splits, int &chunk) {
   const int nqt = attn_tiles(rs, H, Hkv), qg = aw_group(nqt);
   const long wgs = (long)((nqt + qg - 1) / qg) * rs.B * Hkv;
@@ -290,27 +291,29 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   }
 }
 
-// Many-query variant (block refresh, steps of wide blocks): 2 QT waves per workgroup, all of the
-// same (batch row, K/V head): QT query tiles of 32 queries (4, or 2 when a pair has only two or
-// three), each run by two waves that take alternate 32-key tiles (key half 0 the even ones,
-// key half 1 the odd ones); with QT = 4 every SIMD holds two waves and one wave's MFMAs overlap
-// the other's softmax and LDS reads.  Each iteration brings one pair of
-// key tiles (K and V^T, hi and lo) straight from global memory into one of two LDS slots
-// (global_load_lds, 16 bytes per lane, no register staging) while the waves work on the other
-// slot; one barrier per iteration.  At the end the two waves of a query tile merge their
-// (reference maximum, sum, output) through LDS.  In a tile, row r's 16-byte chunk c sits at chunk
+// Many-query variant (block refresh, steps of wide blocks): QT KH waves per workgroup, all of
+// the same (batch row, K/V head): QT query tiles of 32 queries (4, or 2 when a pair has only two
+// or three).  With QT = 4 each query tile is run by KH = 2 waves that take alternate 32-key tiles
+// (key half 0 the even ones, key half 1 the odd ones), so every SIMD holds two waves and one
+// wave's MFMAs overlap the other's softmax and LDS reads.  With QT = 2 (KH = 1) each query
+// tile's wave takes every key tile: the workgroup needs half the LDS, so two fit a CU (in the
+// long-context cached step, 64 queries x 5120 keys per pair, 555 -> 500 us against key halves,
+// whose 128 KB workgroups ran one per CU).  Each iteration brings KH key tiles (K and V^T, hi and
+// lo) straight from global memory into one of two LDS slots (global_load_lds, 16 bytes per lane,
+// no register staging) while the waves work on the other slot; one barrier per iteration.  At
+// the end the two waves of a query tile (KH = 2) merge their (reference maximum, sum, output)
+// through LDS.  In a tile, row r's 16-byte chunk c sits at chunk
 // position r * CPR + (c ^ f(r)) (CPR chunks per row: f(r) = r & 15 for 16, (r >> 1) & 7 for 8,
 // (r >> 2) & 3 for 4), so the fragment reads of 16 consecutive rows cover the 64 banks (256
 // bytes) of the LDS once.  When the workgroups cannot fill the GPU the keys are split into chunks
 // (partials + the merge kernel).
-static constexpr int AW_KH = 2;  // key halves
 
 __device__ inline int aw_swz(int r, int cpr) {
   return cpr >= 16 ? (r & 15) : cpr == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-template <int HD, int QT>
-__global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
+template <int HD, int QT, int KH>
+__global__ __launch_bounds__(64 * QT * KH, 1) void attn_wide_kernel(
     const bf16 *__restrict__ q_hi, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k_hi,
     const bf16 *__restrict__ k_lo, const bf16 *__restrict__ vt_hi, const bf16 *__restrict__ vt_lo,
     RowSet rs, int H, int Hkv, int chunk, float scale_log2, bf16 *o_hi, bf16 *o_lo, float *part,
@@ -318,15 +321,15 @@ __global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
   constexpr int KS = HD / 16, DB = HD / 32;
   constexpr int PLANE = 32 * HD * 2;          // bytes of one plane of a 32-key tile
   constexpr int TILE = 4 * PLANE;             // K hi, K lo, V^T hi, V^T lo
-  constexpr int PAIR = AW_KH * TILE;          // the tiles of one iteration, one per key half
-  constexpr int NW = QT * AW_KH;
+  constexpr int PAIR = KH * TILE;          // the tiles of one iteration, one per key half
+  constexpr int NW = QT * KH;
   constexpr int LPW = PAIR / 1024 / NW;       // 1 KB loads per wave per iteration
   constexpr int KCPR = HD / 8, VCPR = 4;      // 16-byte chunks per K row / per V^T row
   static_assert(PAIR % (1024 * NW) == 0 && LPW >= 1 && LPW <= 32, "tile staging");
   static_assert(LPW * 64 * QT == TILE / 16, "the waves of key half h load tile h");
   // the merge of the key halves reuses the ring: outputs [query tile][d][i][lane], then
   // (reference maximum, sum) [query tile][2][lane]
-  static_assert(QT * (DB * 16 + 2) * 64 * 4 <= 2 * PAIR, "merge area");
+  static_assert(KH == 1 || QT * (DB * 16 + 2) * 64 * 4 <= 2 * PAIR, "merge area");
   typedef __attribute__((address_space(3))) void lds_void;
   __shared__ __align__(1024) unsigned char lds[2 * PAIR];
 
@@ -378,10 +381,10 @@ __global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
   }
   const int ntile = (rs.L + 31) / 32;
   const int t0 = split * (chunk / 32), t1 = min(ntile, t0 + chunk / 32), T = t1 - t0;
-  const int NI = (T + AW_KH - 1) / AW_KH;  // iterations
+  const int NI = (T + KH - 1) / KH;  // iterations
   auto issue = [&](int u) {  // tile t0 + 2u + kh (clamped to the last) into slot u % 2
     unsigned char *dst = lds + (u & 1) * PAIR + wave * LPW * 1024;
-    const size_t kb = (size_t)(t0 + min(u * AW_KH + kh, T - 1)) * 32;
+    const size_t kb = (size_t)(t0 + min(u * KH + kh, T - 1)) * 32;
 #pragma unroll
     for (int j = 0; j < LPW; ++j)
       __builtin_amdgcn_global_load_lds((const void *)(src[j] + kb * HD), (lds_void *)(dst + j * 1024), 16, 0, 0);
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (u + 1 < NI) issue(u + 1);
-    const int tl = u * AW_KH + kh;  // this wave's tile, counted from t0
+    const int tl = u * KH + kh;  // this wave's tile, counted from t0
     const bool tok = tl < T;        // the odd count's last pair has one tile
     const int kb = (t0 + tl) * 32;
     const unsigned char *cur = lds + (u & 1) * PAIR + kh * TILE;
@@ -488,6 +491,7 @@ __global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
     }
   }
   // merge the key halves: half 1 hands its state to half 0 through the (now idle) ring
+  if constexpr (KH == 2) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
   __syncthreads();
   float *xo = (float *)lds;
@@ -513,6 +517,9 @@ __global__ __launch_bounds__(64 * QT * AW_KH, 1) void attn_wide_kernel(
     for (int d = 0; d < DB; ++d)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] = o[d][i] * a1 + xo[((qw * DB + d) * 16 + i) * 64 + lane] * a2;
+  }
+  } else {
+    if (!valid) return;
   }
   if (gridDim.z == 1) {
     const float inv = 1.0f / lsum;
@@ -671,7 +678,8 @@ hipError_t launch_attention(const void *q, const void *q_lo, const void *k_cache
     const int groups = (nqt + qg - 1) / qg;
     dim3 wgrid(attn_grid_x(rs.B * Hkv, groups), 1, wsplits);
 #define ATTNW_LAUNCH(HDV, QTV)                                                                   \
-  hipLaunchKernelGGL((attn_wide_kernel<HDV, QTV>), wgrid, dim3(64 * QTV * AW_KH), 0, st,         \
+  hipLaunchKernelGGL((attn_wide_kernel<HDV, QTV, (QTV == 4 ? 2 : 1)>), wgrid,                   \
+                     dim3(64 * QTV * (QTV == 4 ? 2 : 1)), 0, st,                                 \
                      (const bf16 *)q, (const bf16 *)q_lo, (const bf16 *)k_cache,                \
                      (const bf16 *)k_cache_lo, (const bf16 *)vt_cache, (const bf16 *)vt_cache_lo, \
                      rs, H, Hkv, wchunk, scale_log2, o_hi, o_lo, part, o_packed)
