@@ -296,9 +296,10 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
 // or three).  With QT = 4 each query tile is run by KH = 2 waves that take alternate 32-key tiles
 // (key half 0 the even ones, key half 1 the odd ones), so every SIMD holds two waves and one
 // wave's MFMAs overlap the other's softmax and LDS reads.  With QT = 2 (KH = 1) each query
-// tile's wave takes every key tile: the workgroup needs half the LDS, so two fit a CU (in the
-// long-context cached step, 64 queries x 5120 keys per pair, 555 -> 500 us against key halves,
-// whose 128 KB workgroups ran one per CU).  Each iteration brings KH key tiles (K and V^T, hi and
+// tile's wave takes every key tile: the workgroup needs half the LDS, so two fit a CU (64
+// queries x 5120 keys per pair: 555 -> 500 us against key halves, whose 128 KB workgroups ran
+// one per CU, when launched alone; within the decode's noise in the long-context cached step).
+// Each iteration brings KH key tiles (K and V^T, hi and
 // lo) straight from global memory into one of two LDS slots (global_load_lds, 16 bytes per lane,
 // no register staging) while the waves work on the other slot; one barrier per iteration.  At
 // the end the two waves of a query tile (KH = 2) merge their (reference maximum, sum, output)
